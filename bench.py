@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = the whole path over one batch of resident synthetic inputs:
+fa_fwd (forward kernel) followed by the three backward kernels (rowsum(dO.O),
+dK/dV, dQ), each launched through the C ABI on torch's current stream.
+
+Default workload: long-context causal fp16 attention, B=1, H=16,
+S=16384, D=128, Q/K/V/dO iid N(0,1) rounded to fp16.
+
+FLOP accounting: forward = 4*B*H*Sq*Sk*D, halved when causal ("FlashAttention-2
+from PyTorch to Triton", the benchmark harness's attn_flops); forward+backward
+= 3.5x forward (backward counted as 2.5x forward).  The roofline object
+reports the dominant kernel against the dense fp16 MFMA peak of MI355X.
+
+Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one
+GPU only (attention heads shard across GPUs with no communication).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+MFMA_PEAK_F16 = 2516.6  # TFLOP/s, dense fp16, MI355X (256 CU x 4096 flop/clk x 2.4 GHz)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1,
+                    help="heads of the workload the CPU oracle times (bounded sample)")
+    ap.add_argument("--sweep", default="",
+                    help="optional path: also time the fp16 length sweep and write JSON lines there")
+    return ap.parse_args()
+
+
+def fwd_flops(B, H, Sq, Sk, D, causal):
+    f = 4.0 * B * H * Sq * Sk * D
+    return f / 2 if causal else f
+
+
+def make_device_inputs(case, torch):
+    from exact_attention_88_amd import workloads as W
+    x = W.make_inputs(case)
+    dev = {n: torch.from_numpy(a.copy()).to("cuda") for n, a in x.items()}
+    return x, dev
+
+
+def time_path(fa, torch, case, dev, steps, warmup):
+    """Time `steps` full passes; per-kernel durations from HIP events recorded
+    on the stream the kernels run on (torch's current stream)."""
+    B, H, Sq, Sk, D = case.B, case.H, case.Sq, case.Sk, case.D
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+    sc = case.scale
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_fwd(q, k, v, case.causal, sc, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        for stage in (0, 1, 2):
+            fa.fa_bwd_stage(stage, -1, q, k, v, o, do, lse, case.causal, sc, dq=dq, dk=dk, dv=dv,
+                            delta=delta)
+            if ev is not None:
+                ev[2 + stage].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+    per = {n: [] for n in names}
+    for ev in evs:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]))
+    avg = {n: sum(v) / len(v) for n, v in per.items()}
+    return wall, avg
+
+
+def cpu_baseline(case, x, heads):
+    """The CPU oracle, as it stands, on `heads` heads of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    for hh in range(heads):
+        h = hh % case.H
+        q, k, v, do = (np.asarray(x[n][0, h]) for n in ("q", "k", "v", "do"))
+        oracle.head_forward(q, k, v, case.scale, case.causal)
+        oracle.head_backward(q, k, v, do, case.scale, case.causal)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * fwd_flops(1, heads, case.Sq, case.Sk, case.D, case.causal)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{heads} of {case.B * case.H} heads (b=0) of the same workload, forward + "
+                       f"backward, float64 numpy materialised attention, {dt:.1f} s; TFLOP/s under "
+                       f"the same causal accounting as the GPU figure")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(heads would shard across GPUs with no communication)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from exact_attention_88_amd import fa
+    from exact_attention_88_amd import workloads as W
+
+    case = W.long_case()
+    x, dev = make_device_inputs(case, torch)
+    wall, avg = time_path(fa, torch, case, dev, args.steps, args.warmup)
+    ff = fwd_flops(case.B, case.H, case.Sq, case.Sk, case.D, case.causal)
+    ms_step = wall / args.steps * 1e3
+    value = 3.5 * ff / (wall / args.steps) / 1e12
+    fwd_tf = ff / (avg["fwd"] * 1e-3) / 1e12
+    # Dominant kernel: the longest average launch.  Algorithmic flops per launch:
+    # forward = 2 matmul units (QK^T, PV), dK/dV = 4 (S, dV, dP, dK), dQ = 3
+    # (S, dP, dQ); one unit = 2*B*H*Sq*Sk*D flops (halved when causal).
+    unit = ff / 2
+    units = {"fwd": 2, "bwd_dkdv": 4, "bwd_dq": 3}
+    dom = max(units, key=lambda n: avg[n])
+    achieved = units[dom] * unit / (avg[dom] * 1e-3) / 1e12
+    line = {
+        "metric": "attention TFLOP/s fwd+bwd (fp16, causal, D=128)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic: Q,K,V,dO iid N(0,1) rounded to fp16, seed 4",
+        "config": {"workload": "long-context causal fp16 attention fwd+bwd, B=1 H=16 S=16384 D=128",
+                   "B": case.B, "H": case.H, "S": case.Sq, "D": case.D, "causal": True},
+        "fwd_tflops": round(fwd_tf, 2),
+        "fwd_frac_of_peak": round(fwd_tf / MFMA_PEAK_F16, 4),
+        "fwdbwd_frac_of_peak": round(value / MFMA_PEAK_F16, 4),
+        "kernel_ms": {n: round(v, 4) for n, v in avg.items()},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": MFMA_PEAK_F16, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_F16, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, x, args.cpu_heads)
+    if args.sweep:
+        with open(args.sweep, "w") as f:
+            for sc in W.sweep_cases():
+                xs, ds = make_device_inputs(sc, torch)
+                w2, a2 = time_path(fa, torch, sc, ds, max(3, args.steps // 2), 2)
+                f2 = fwd_flops(sc.B, sc.H, sc.Sq, sc.Sk, sc.D, sc.causal)
+                rec = {"case": sc.name, "S": sc.Sq, "B": sc.B, "causal": sc.causal,
+                       "fwd_tflops": f2 / (a2["fwd"] * 1e-3) / 1e12,
+                       "fwdbwd_tflops": 3.5 * f2 / (w2 / max(3, args.steps // 2)) / 1e12,
+                       "kernel_ms": a2}
+                f.write(json.dumps(rec) + "\n")
+                print(f"[sweep] {json.dumps(rec)}", file=sys.stderr, flush=True)
+                del ds
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

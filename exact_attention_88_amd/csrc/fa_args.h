@@ -1,0 +1,65 @@
+// Kernel argument blocks and launcher declarations shared by the host entry
+// points (fa_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// A logical [B, H, S, D] tensor: base pointer and element strides.
+struct T4 {
+  const void* p;
+  int64_t sb, sh, ss, sd;
+};
+
+enum : int {
+  VEC_Q = 1, VEC_K = 2, VEC_V = 4, VEC_O = 8, VEC_DO = 16, VEC_DQ = 32, VEC_DK = 64, VEC_DV = 128
+};
+
+struct FwdArgs {
+  T4 q, k, v, o;
+  float* lse;
+  int B, H, Sq, Sk;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  int vec;           // VEC_* bits: 16-byte vector access allowed per tensor
+};
+
+struct BwdArgs {
+  T4 q, k, v, o, dout, dq, dk, dv;
+  const float* lse;
+  float* delta;
+  int B, H, Sq, Sk;
+  float scale;       // softmax scale (applied to dq, dk)
+  float scale_log2;  // scale * log2(e)
+  int vec;
+};
+
+struct TileCfg {
+  int bm;     // query rows per workgroup (forward, dq) / per inner step (dk/dv)
+  int bn;     // keys per inner step (forward, dq) / per workgroup (dk/dv)
+  int waves;  // wavefronts per workgroup
+  int lds;    // static LDS bytes
+};
+
+// Per-pass tile tables (index = tile id) for a dtype (0 = f16, 1 = f32) and
+// head dim; count returns the number of entries.
+int fwd_tile_count(int dtype, int D);
+const TileCfg* fwd_tile(int dtype, int D, int id);
+int fwd_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal);
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s);
+
+int dkdv_tile_count(int dtype, int D);
+const TileCfg* dkdv_tile(int dtype, int D, int id);
+int dkdv_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal);
+hipError_t launch_dkdv(const BwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s);
+
+int dq_tile_count(int dtype, int D);
+const TileCfg* dq_tile(int dtype, int D, int id);
+int dq_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal);
+hipError_t launch_dq(const BwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s);
+
+hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int D, hipStream_t s);
+
+}  // namespace fa

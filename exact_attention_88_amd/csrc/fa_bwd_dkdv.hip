@@ -1,0 +1,328 @@
+// Backward dK/dV kernel for gfx950, and the rowsum(dO.O) preprocess.
+//
+// Method ("Triton FlashAttention": the backward split the FlashAttention-2
+// way into a dK/dV kernel and a dQ kernel with no atomics, probabilities
+// rebuilt from the saved log-sum-exp, rowsum(dO.O) in its own small kernel;
+// "FlashAttention-2 from PyTorch to Triton", the backward outline: L, the
+// precomputed D = rowsum(dO o O) and a loop over query tiles per key tile).
+//
+// One workgroup owns BN = 32*waves keys of one (batch, head); each wave keeps
+// its 32 keys' K and V fragments in registers and accumulates dK^T and dV^T
+// (fp32) while query tiles of BM rows (Q, dO, LSE, delta) stream through LDS.
+// Per 32-query block:
+//   S  = Q K^T            (C layout: lane = key, registers = queries)
+//   P  = exp2(S*scale*log2e - LSE*log2e)
+//   dV^T += dO^T P        (dO^T read transposed from LDS)
+//   dP = dO V^T
+//   dS = P o (dP - delta)
+//   dK^T += Q^T dS        (Q^T read transposed from LDS)
+// and dK is scaled by `scale` on the way out.  Each output row is written by
+// exactly one workgroup.
+#include "fa_args.h"
+#include "fa_common.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kLdsMax = 65536;
+
+// ----------------------------------------------------------------- preprocess
+// delta[bh, i] = sum_d dO[i, d] * O[i, d] in fp32.  G threads share a row,
+// each reading 16-byte chunks.
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
+  constexpr int CH = 16 / (int)sizeof(T);
+  constexpr int G = D / CH;  // threads per row (power of two, <= 32)
+  constexpr int RPB = 256 / G;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / G;
+  const int part = threadIdx.x % G;
+  const int64_t nrows = (int64_t)a.B * a.H * a.Sq;
+  float acc = 0.f;
+  if (row < nrows) {
+    const int64_t bh = row / a.Sq;
+    const int i = (int)(row - bh * a.Sq);
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const T* orow = (const T*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)i * a.o.ss;
+    const T* drow = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh + (int64_t)i * a.dout.ss;
+    const int col = part * CH;
+    T ov[CH], dv[CH];
+    if (a.vec & VEC_O) {
+      __builtin_memcpy(ov, orow + col, 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < CH; ++e) ov[e] = orow[(int64_t)(col + e) * a.o.sd];
+    }
+    if (a.vec & VEC_DO) {
+      __builtin_memcpy(dv, drow + col, 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < CH; ++e) dv[e] = drow[(int64_t)(col + e) * a.dout.sd];
+    }
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc = __builtin_fmaf((float)dv[e], (float)ov[e], acc);
+  }
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < nrows && part == 0) a.delta[row] = acc;
+}
+
+// ----------------------------------------------------------------- dK / dV
+struct Tile { int bm, nw; };
+constexpr Tile kTilesH[] = {{64, 4}, {32, 4}, {64, 2}, {128, 4}, {32, 8}};
+constexpr Tile kTilesF[] = {{32, 4}, {32, 2}, {64, 4}};
+constexpr int kNumH = sizeof(kTilesH) / sizeof(kTilesH[0]);
+constexpr int kNumF = sizeof(kTilesF) / sizeof(kTilesF[0]);
+
+constexpr int lds_bytes(int esize, int D, int bm) {
+  return 2 * bm * ((D < 32 ? 32 : D) + 16 / esize) * esize + 2 * bm * 4;
+}
+constexpr Tile tile_at(int dt, int i) { return dt == 0 ? kTilesH[i] : kTilesF[i]; }
+constexpr int num_tiles_raw(int dt) { return dt == 0 ? kNumH : kNumF; }
+constexpr bool tile_ok(int dt, int D, int i) {
+  return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bm) <= kLdsMax;
+}
+constexpr int raw_index(int dt, int D, int id) {
+  int n = 0;
+  for (int i = 0; i < num_tiles_raw(dt); ++i) {
+    if (tile_ok(dt, D, i)) {
+      if (n == id) return i;
+      ++n;
+    }
+  }
+  return -1;
+}
+constexpr int count_ok(int dt, int D) {
+  int n = 0;
+  for (int i = 0; i < num_tiles_raw(dt); ++i) n += tile_ok(dt, D, i) ? 1 : 0;
+  return n;
+}
+
+template <class T, int D, int BM, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
+  typedef Mfma<T> M;
+  constexpr int BN = 32 * NW;
+  constexpr int NT = NW * 64;
+  constexpr int LS = LdsRow<T, D>::LS;
+  constexpr int NKS = D / M::KSTEP;
+  constexpr int NDB = (D + 31) / 32;
+  constexpr int NQB = BM / 32;
+  constexpr int TPB = 32 / M::KSTEP;
+  __shared__ __attribute__((aligned(16))) T Qs[BM * LS];
+  __shared__ __attribute__((aligned(16))) T Ds[BM * LS];
+  __shared__ float Ls[BM];
+  __shared__ float Dl[BM];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
+  const int nkb = (a.Sk + BN - 1) / BN;
+  const int kb = blockIdx.x % nkb;
+  const int bh = blockIdx.x / nkb;
+  const int b = bh / a.H, h = bh % a.H;
+  const int k0 = kb * BN, kw = k0 + w * 32, kj = kw + c;
+
+  const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
+  const T* kbase = (const T*)a.k.p + b * a.k.sb + h * a.k.sh;
+  const T* vbase = (const T*)a.v.p + b * a.v.sb + h * a.v.sh;
+  const T* dobase = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh;
+  const float* lse = a.lse + (int64_t)bh * a.Sq;
+  const float* dl = a.delta + (int64_t)bh * a.Sq;
+
+  typename M::frag kf[NKS], vf[NKS];
+  load_row_frags<T, D>(kf, kbase, a.k.ss, a.k.sd, kj, a.Sk, a.vec & VEC_K);
+  load_row_frags<T, D>(vf, vbase, a.v.ss, a.v.sd, kj, a.Sk, a.vec & VEC_V);
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) { dk[i] = zero16(); dv[i] = zero16(); }
+  const float cs = a.scale_log2;
+  const bool vecq = a.vec & VEC_Q, vecd = a.vec & VEC_DO;
+  const bool key_tail = k0 + BN > a.Sk;
+
+  const int qstart = CAUSAL ? (k0 / BM) * BM : 0;
+  for (int q0 = qstart; q0 < a.Sq; q0 += BM) {
+    __syncthreads();
+    load_tile<T, BM, D, LS, NT>(Qs, qbase, a.q.ss, a.q.sd, q0, a.Sq, vecq);
+    load_tile<T, BM, D, LS, NT>(Ds, dobase, a.dout.ss, a.dout.sd, q0, a.Sq, vecd);
+    for (int r = threadIdx.x; r < BM; r += NT) {
+      const int i = q0 + r;
+      // fp16 kernels use LSE*log2(e); fp32 kernels use LSE itself.
+      Ls[r] = i < a.Sq ? (sizeof(T) == 2 ? lse[i] * kLog2e : lse[i]) : INFINITY;
+      Dl[r] = i < a.Sq ? dl[i] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qs = q0 + qb * 32;
+      if (CAUSAL && qs + 31 < kw) continue;  // every query of the block precedes every key
+      f32x16 s = dot_block<T, D, LS>(Qs, qb * 32, kf);
+      const bool need_mask = key_tail || (CAUSAL && qs < kw + 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = qb * 32 + crow(r, g);
+        float p;
+        if constexpr (sizeof(T) == 2)
+          p = fast_exp2(__builtin_fmaf(s[r], cs, -Ls[qr]));
+        else
+          p = fast_exp2(__builtin_fmaf(a.scale, s[r], -Ls[qr]) * kLog2e);
+        if (need_mask && (kj >= a.Sk || (CAUSAL && kj > q0 + qr))) p = 0.f;
+        s[r] = p;
+      }
+#pragma unroll
+      for (int tt = 0; tt < TPB; ++tt) {
+        const typename M::frag pf = frag_from_acc<T>(s, tt);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dv[db] = M::mma(frag_tr<T, LS>(Ds, qb * 32, tt, db * 32), pf, dv[db]);
+      }
+      const f32x16 dp = dot_block<T, D, LS>(Ds, qb * 32, vf);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = qb * 32 + crow(r, g);
+        s[r] = s[r] * (dp[r] - Dl[qr]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < TPB; ++tt) {
+        const typename M::frag df = frag_from_acc<T>(s, tt);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dk[db] = M::mma(frag_tr<T, LS>(Qs, qb * 32, tt, db * 32), df, dk[db]);
+      }
+    }
+  }
+
+  if (kj < a.Sk) {
+    T* dkrow = (T*)a.dk.p + b * a.dk.sb + h * a.dk.sh + (int64_t)kj * a.dk.ss;
+    T* dvrow = (T*)a.dv.p + b * a.dv.sb + h * a.dv.sh + (int64_t)kj * a.dv.ss;
+    const bool veck = a.vec & VEC_DK, vecv = a.vec & VEC_DV;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float k4[4], v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = dk[db][r4 * 4 + e] * a.scale;
+          v4[e] = dv[db][r4 * 4 + e];
+        }
+        store4<T, D>(dkrow, a.dk.sd, db * 32 + r4 * 8 + g * 4, k4, veck);
+        store4<T, D>(dvrow, a.dv.sd, db * 32 + r4 * 8 + g * 4, v4, vecv);
+      }
+  }
+}
+
+template <class T, int D, int I, bool CAUSAL>
+hipError_t launch_one(const BwdArgs& a, hipStream_t s) {
+  constexpr int dt = sizeof(T) == 2 ? 0 : 1;
+  constexpr Tile tl = tile_at(dt, I);
+  constexpr int BN = 32 * tl.nw;
+  const int64_t nkb = ((int64_t)a.Sk + BN - 1) / BN;
+  const int64_t grid = nkb * a.B * a.H;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_kernel<T, D, tl.bm, tl.nw, CAUSAL>), dim3((unsigned)grid), dim3(tl.nw * 64), args, 0, s);
+}
+
+template <class T, int D, int I = 0>
+hipError_t dispatch(const BwdArgs& a, int raw, int causal, hipStream_t s) {
+  constexpr int dt = sizeof(T) == 2 ? 0 : 1;
+  if constexpr (I >= num_tiles_raw(dt)) {
+    return hipErrorInvalidValue;
+  } else {
+    if (raw == I) {
+      if constexpr (tile_ok(dt, D, I)) {
+        return causal ? launch_one<T, D, I, true>(a, s) : launch_one<T, D, I, false>(a, s);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    }
+    return dispatch<T, D, I + 1>(a, raw, causal, s);
+  }
+}
+
+int raw_for(int dtype, int D, int id) {
+  switch (D) {
+    case 16: return raw_index(dtype, 16, id);
+    case 32: return raw_index(dtype, 32, id);
+    case 64: return raw_index(dtype, 64, id);
+    case 128: return raw_index(dtype, 128, id);
+  }
+  return -1;
+}
+
+template <class T, int D>
+hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
+  constexpr int G = D / (16 / (int)sizeof(T));
+  constexpr int RPB = 256 / G;
+  const int64_t rows = (int64_t)a.B * a.H * a.Sq;
+  const int64_t grid = (rows + RPB - 1) / RPB;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_pre_kernel<T, D>), dim3((unsigned)grid), dim3(256), args, 0, s);
+}
+
+}  // namespace
+
+int dkdv_tile_count(int dtype, int D) {
+  switch (D) {
+    case 16: return count_ok(dtype, 16);
+    case 32: return count_ok(dtype, 32);
+    case 64: return count_ok(dtype, 64);
+    case 128: return count_ok(dtype, 128);
+  }
+  return 0;
+}
+
+const TileCfg* dkdv_tile(int dtype, int D, int id) {
+  static thread_local TileCfg cfg;
+  if (id < 0 || id >= dkdv_tile_count(dtype, D)) return nullptr;
+  const Tile t = tile_at(dtype, raw_for(dtype, D, id));
+  cfg = TileCfg{t.bm, 32 * t.nw, t.nw, lds_bytes(dtype == 0 ? 2 : 4, D, t.bm)};
+  return &cfg;
+}
+
+int dkdv_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
+  (void)dtype; (void)D; (void)Sq; (void)Sk; (void)causal;
+  return 0;
+}
+
+hipError_t launch_dkdv(const BwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s) {
+  const int raw = raw_for(dtype, D, tile);
+  if (raw < 0) return hipErrorInvalidValue;
+  if (dtype == 0) {
+    switch (D) {
+      case 16: return dispatch<half_t, 16>(a, raw, causal, s);
+      case 32: return dispatch<half_t, 32>(a, raw, causal, s);
+      case 64: return dispatch<half_t, 64>(a, raw, causal, s);
+      case 128: return dispatch<half_t, 128>(a, raw, causal, s);
+    }
+  } else {
+    switch (D) {
+      case 16: return dispatch<float, 16>(a, raw, causal, s);
+      case 32: return dispatch<float, 32>(a, raw, causal, s);
+      case 64: return dispatch<float, 64>(a, raw, causal, s);
+      case 128: return dispatch<float, 128>(a, raw, causal, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int D, hipStream_t s) {
+  if (dtype == 0) {
+    switch (D) {
+      case 16: return launch_pre_t<half_t, 16>(a, s);
+      case 32: return launch_pre_t<half_t, 32>(a, s);
+      case 64: return launch_pre_t<half_t, 64>(a, s);
+      case 128: return launch_pre_t<half_t, 128>(a, s);
+    }
+  } else {
+    switch (D) {
+      case 16: return launch_pre_t<float, 16>(a, s);
+      case 32: return launch_pre_t<float, 32>(a, s);
+      case 64: return launch_pre_t<float, 64>(a, s);
+      case 128: return launch_pre_t<float, 128>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

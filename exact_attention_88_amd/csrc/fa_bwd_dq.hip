@@ -1,0 +1,236 @@
+// Backward dQ kernel for gfx950.
+//
+// Method ("Triton FlashAttention": the dQ kernel of the FlashAttention-2
+// backward split, one program per query block looping over key blocks, so
+// that nothing needs atomics; probabilities rebuilt from the saved
+// log-sum-exp).
+//
+// One workgroup owns BM = 32*waves query rows of one (batch, head); each wave
+// keeps its 32 rows' Q and dO fragments, LSE and delta in registers and
+// accumulates dQ^T (fp32) while K and V tiles of BN keys stream through LDS.
+// Per 32-key block, computed transposed so that each lane owns one query:
+//   S^T  = K Q^T
+//   P^T  = exp2(S^T*scale*log2e - LSE*log2e)
+//   dP^T = V dO^T
+//   dS^T = P^T o (dP^T - delta)
+//   dQ^T += K^T dS^T      (K^T read transposed from LDS)
+// and dQ is scaled by `scale` on the way out.
+#include "fa_args.h"
+#include "fa_common.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kLdsMax = 65536;
+
+struct Tile { int bn, nw; };
+constexpr Tile kTilesH[] = {{64, 4}, {32, 4}, {64, 2}, {128, 4}, {64, 8}};
+constexpr Tile kTilesF[] = {{32, 4}, {32, 2}, {64, 4}};
+constexpr int kNumH = sizeof(kTilesH) / sizeof(kTilesH[0]);
+constexpr int kNumF = sizeof(kTilesF) / sizeof(kTilesF[0]);
+
+constexpr int lds_bytes(int esize, int D, int bn) {
+  return 2 * bn * ((D < 32 ? 32 : D) + 16 / esize) * esize;
+}
+constexpr Tile tile_at(int dt, int i) { return dt == 0 ? kTilesH[i] : kTilesF[i]; }
+constexpr int num_tiles_raw(int dt) { return dt == 0 ? kNumH : kNumF; }
+constexpr bool tile_ok(int dt, int D, int i) {
+  return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bn) <= kLdsMax;
+}
+constexpr int raw_index(int dt, int D, int id) {
+  int n = 0;
+  for (int i = 0; i < num_tiles_raw(dt); ++i) {
+    if (tile_ok(dt, D, i)) {
+      if (n == id) return i;
+      ++n;
+    }
+  }
+  return -1;
+}
+constexpr int count_ok(int dt, int D) {
+  int n = 0;
+  for (int i = 0; i < num_tiles_raw(dt); ++i) n += tile_ok(dt, D, i) ? 1 : 0;
+  return n;
+}
+
+template <class T, int D, int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
+  typedef Mfma<T> M;
+  constexpr int BM = 32 * NW;
+  constexpr int NT = NW * 64;
+  constexpr int LS = LdsRow<T, D>::LS;
+  constexpr int NKS = D / M::KSTEP;
+  constexpr int NDB = (D + 31) / 32;
+  constexpr int NKB = BN / 32;
+  constexpr int TPB = 32 / M::KSTEP;
+  __shared__ __attribute__((aligned(16))) T Ks[BN * LS];
+  __shared__ __attribute__((aligned(16))) T Vs[BN * LS];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
+  const int nqb = (a.Sq + BM - 1) / BM;
+  int qb = blockIdx.x % nqb;
+  const int bh = blockIdx.x / nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+  const int b = bh / a.H, h = bh % a.H;
+  const int q0 = qb * BM, qw = q0 + w * 32, qi = qw + c;
+
+  const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
+  const T* kbase = (const T*)a.k.p + b * a.k.sb + h * a.k.sh;
+  const T* vbase = (const T*)a.v.p + b * a.v.sb + h * a.v.sh;
+  const T* dobase = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh;
+
+  typename M::frag qf[NKS], df[NKS];
+  load_row_frags<T, D>(qf, qbase, a.q.ss, a.q.sd, qi, a.Sq, a.vec & VEC_Q);
+  load_row_frags<T, D>(df, dobase, a.dout.ss, a.dout.sd, qi, a.Sq, a.vec & VEC_DO);
+  const bool valid = qi < a.Sq;
+  // fp16 uses LSE*log2(e) in one FMA per score; fp32 uses LSE itself (see below).
+  const float lse_n = valid ? a.lse[(int64_t)bh * a.Sq + qi] : INFINITY;
+  const float lse2 = sizeof(T) == 2 ? lse_n * kLog2e : lse_n;
+  const float dlt = valid ? a.delta[(int64_t)bh * a.Sq + qi] : 0.f;
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dq[i] = zero16();
+  const float cs = a.scale_log2;
+  const bool veck = a.vec & VEC_K, vecv = a.vec & VEC_V;
+
+  const int kend = CAUSAL ? min(a.Sk, q0 + BM) : a.Sk;
+  const int ntiles = (kend + BN - 1) / BN;
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    __syncthreads();
+    load_tile<T, BN, D, LS, NT>(Ks, kbase, a.k.ss, a.k.sd, k0, a.Sk, veck);
+    load_tile<T, BN, D, LS, NT>(Vs, vbase, a.v.ss, a.v.sd, k0, a.Sk, vecv);
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int ks0 = k0 + kb * 32;
+      if (CAUSAL && ks0 > qw + 31) continue;  // block entirely after this wave's rows
+      f32x16 s = dot_block<T, D, LS>(Ks, kb * 32, qf);
+      const bool need_mask = (ks0 + 32 > a.Sk) || (CAUSAL && ks0 + 31 > qw);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = ks0 + crow(r, g);
+        float p;
+        if constexpr (sizeof(T) == 2)
+          p = fast_exp2(__builtin_fmaf(s[r], cs, -lse2));
+        else
+          p = fast_exp2(__builtin_fmaf(a.scale, s[r], -lse2) * kLog2e);
+        if (need_mask && (key >= a.Sk || (CAUSAL && key > qi))) p = 0.f;
+        s[r] = p;
+      }
+      const f32x16 dp = dot_block<T, D, LS>(Vs, kb * 32, df);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - dlt);
+#pragma unroll
+      for (int tt = 0; tt < TPB; ++tt) {
+        const typename M::frag sf = frag_from_acc<T>(s, tt);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dq[db] = M::mma(frag_tr<T, LS>(Ks, kb * 32, tt, db * 32), sf, dq[db]);
+      }
+    }
+  }
+
+  if (valid) {
+    T* row = (T*)a.dq.p + b * a.dq.sb + h * a.dq.sh + (int64_t)qi * a.dq.ss;
+    const bool vecq = a.vec & VEC_DQ;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = dq[db][r4 * 4 + e] * a.scale;
+        store4<T, D>(row, a.dq.sd, db * 32 + r4 * 8 + g * 4, v4, vecq);
+      }
+  }
+}
+
+template <class T, int D, int I, bool CAUSAL>
+hipError_t launch_one(const BwdArgs& a, hipStream_t s) {
+  constexpr int dt = sizeof(T) == 2 ? 0 : 1;
+  constexpr Tile tl = tile_at(dt, I);
+  constexpr int BM = 32 * tl.nw;
+  const int64_t nqb = ((int64_t)a.Sq + BM - 1) / BM;
+  const int64_t grid = nqb * a.B * a.H;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_kernel<T, D, tl.bn, tl.nw, CAUSAL>), dim3((unsigned)grid), dim3(tl.nw * 64), args, 0, s);
+}
+
+template <class T, int D, int I = 0>
+hipError_t dispatch(const BwdArgs& a, int raw, int causal, hipStream_t s) {
+  constexpr int dt = sizeof(T) == 2 ? 0 : 1;
+  if constexpr (I >= num_tiles_raw(dt)) {
+    return hipErrorInvalidValue;
+  } else {
+    if (raw == I) {
+      if constexpr (tile_ok(dt, D, I)) {
+        return causal ? launch_one<T, D, I, true>(a, s) : launch_one<T, D, I, false>(a, s);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    }
+    return dispatch<T, D, I + 1>(a, raw, causal, s);
+  }
+}
+
+int raw_for(int dtype, int D, int id) {
+  switch (D) {
+    case 16: return raw_index(dtype, 16, id);
+    case 32: return raw_index(dtype, 32, id);
+    case 64: return raw_index(dtype, 64, id);
+    case 128: return raw_index(dtype, 128, id);
+  }
+  return -1;
+}
+
+}  // namespace
+
+int dq_tile_count(int dtype, int D) {
+  switch (D) {
+    case 16: return count_ok(dtype, 16);
+    case 32: return count_ok(dtype, 32);
+    case 64: return count_ok(dtype, 64);
+    case 128: return count_ok(dtype, 128);
+  }
+  return 0;
+}
+
+const TileCfg* dq_tile(int dtype, int D, int id) {
+  static thread_local TileCfg cfg;
+  if (id < 0 || id >= dq_tile_count(dtype, D)) return nullptr;
+  const Tile t = tile_at(dtype, raw_for(dtype, D, id));
+  cfg = TileCfg{32 * t.nw, t.bn, t.nw, lds_bytes(dtype == 0 ? 2 : 4, D, t.bn)};
+  return &cfg;
+}
+
+int dq_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
+  (void)dtype; (void)D; (void)Sq; (void)Sk; (void)causal;
+  return 0;
+}
+
+hipError_t launch_dq(const BwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s) {
+  const int raw = raw_for(dtype, D, tile);
+  if (raw < 0) return hipErrorInvalidValue;
+  if (dtype == 0) {
+    switch (D) {
+      case 16: return dispatch<half_t, 16>(a, raw, causal, s);
+      case 32: return dispatch<half_t, 32>(a, raw, causal, s);
+      case 64: return dispatch<half_t, 64>(a, raw, causal, s);
+      case 128: return dispatch<half_t, 128>(a, raw, causal, s);
+    }
+  } else {
+    switch (D) {
+      case 16: return dispatch<float, 16>(a, raw, causal, s);
+      case 32: return dispatch<float, 32>(a, raw, causal, s);
+      case 64: return dispatch<float, 64>(a, raw, causal, s);
+      case 128: return dispatch<float, 128>(a, raw, causal, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -45,7 +45,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["attention_forward", "attention_backward", "delta_rowsum", "head_forward",
-           "head_backward"]
+           "head_backward", "head_forward_rows", "head_backward_rows"]
 
 ROW_BLOCK = 2048
 
@@ -133,3 +133,54 @@ def attention_backward(q, k, v, do, scale, causal, row_block=ROW_BLOCK):
 def delta_rowsum(do, o):
     """rowsum(dO o O) over the last axis, in float64 (the backward's preprocess)."""
     return (_f64(do) * _f64(o)).sum(axis=-1)
+
+
+def head_forward_rows(q, k, v, scale, causal, rows):
+    """Forward outputs for the given absolute query rows only (each row is the
+    plain definition over its full score row): (o [len(rows), D], lse [len(rows)])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    rows = np.asarray(rows, dtype=np.int64)
+    s = scale * (q[rows] @ k.T)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > rows[:, None], -np.inf, s)
+    L = _lse(s)
+    return np.exp(s - L) @ v, L[:, 0]
+
+
+def head_backward_rows(q, k, v, do, scale, causal, q_rows, k_rows, row_block=ROW_BLOCK):
+    """Gradients for sampled rows: dq at absolute query rows ``q_rows`` and
+    dk, dv at absolute key rows ``k_rows``.
+
+    The softmax term sum_k P_ik dP_ik needs whole rows, so it and LSE are
+    formed for every query row (row_block rows at a time); the sampled
+    gradients then follow the same definitions as ``head_backward``.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    Sq = q.shape[0]
+    lse = np.empty(Sq)
+    psum = np.empty(Sq)
+    for r0 in range(0, Sq, row_block):
+        r1 = min(Sq, r0 + row_block)
+        s = _scores(q[r0:r1], k, scale, causal, r0)
+        L = _lse(s)
+        p = np.exp(s - L)
+        psum[r0:r1] = (p * (do[r0:r1] @ v.T)).sum(axis=1)
+        lse[r0:r1] = L[:, 0]
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    # dq rows: full key range for each sampled query.
+    s = scale * (q[q_rows] @ k.T)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > q_rows[:, None], -np.inf, s)
+    p = np.exp(s - lse[q_rows][:, None])
+    ds = p * (do[q_rows] @ v.T - psum[q_rows][:, None])
+    dq = scale * (ds @ k)
+    # dk, dv rows: full query range for each sampled key (columns of P).
+    s = scale * (q @ k[k_rows].T)
+    if causal:
+        s = np.where(k_rows[None, :] > np.arange(Sq)[:, None], -np.inf, s)
+    p = np.exp(s - lse[:, None])
+    dv = p.T @ do
+    ds = p * (do @ v[k_rows].T - psum[:, None])
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv

@@ -1,0 +1,64 @@
+"""Helpers for the GPU parity tests: device tensors in the workloads' storage
+layouts, NaN-poisoned outputs, and the error measures with their tolerances.
+
+Tolerances (the pages' own ones existed only because of TF32, so the bars here
+are tighter):
+  float32: max |x - ref| <= 2e-5 for O and LSE, <= 1e-4 for dQ, dK, dV;
+  float16: max |x - ref| / max |ref| <= 2e-3 for O and <= 1e-2 for dQ, dK, dV,
+           and max |lse - ref| <= 2e-3 (LSE is float32 from float32 sums).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TOL = {
+    "f32": {"o": 2e-5, "lse": 2e-5, "grad": 1e-4},
+    "f16": {"o": 2e-3, "lse": 2e-3, "grad": 1e-2},
+}
+
+
+def torch_dtype(case_dtype):
+    import torch
+    return torch.float16 if case_dtype == "f16" else torch.float32
+
+
+def to_device(x, device="cuda"):
+    """numpy [B,H,S,D] (possibly a transposed view of [B,S,H,D]) -> torch view
+    with the same logical shape and the same storage order on the device."""
+    import torch
+    if x.flags["C_CONTIGUOUS"]:
+        return torch.from_numpy(np.array(x)).to(device)
+    store = np.ascontiguousarray(x.transpose(0, 2, 1, 3))
+    return torch.from_numpy(store).to(device).transpose(1, 2)
+
+
+def empty_like_layout(shape, dtype, layout, device="cuda", fill=float("nan")):
+    """A NaN-filled output in logical [B,H,S,D] order with the given storage layout."""
+    import torch
+    B, H, S, D = shape
+    if layout == "bhsd":
+        return torch.full((B, H, S, D), fill, dtype=dtype, device=device)
+    return torch.full((B, S, H, D), fill, dtype=dtype, device=device).transpose(1, 2)
+
+
+def nan_vec(shape, device="cuda"):
+    import torch
+    return torch.full(shape, float("nan"), dtype=torch.float32, device=device)
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def err(x, ref, dtype, kind):
+    """Error measure for this dtype and quantity (absolute for f32 and LSE,
+    relative to max |ref| for f16 tensors)."""
+    d = float(np.max(np.abs(x - ref))) if x.size else 0.0
+    if dtype == "f16" and kind != "lse":
+        m = float(np.max(np.abs(ref))) if ref.size else 0.0
+        return d / m if m > 0 else d
+    return d
+
+
+def tol(dtype, kind):
+    return TOL[dtype]["grad" if kind in ("dq", "dk", "dv") else kind]

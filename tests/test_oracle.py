@@ -417,3 +417,21 @@ def test_planted_forward_mistake_is_caught(kind):
                                   "dv_uses_ds"])
 def test_planted_backward_mistake_is_caught(kind):
     assert _any_pin_fails(oracle.head_forward, _mut_backward(kind))
+
+
+def test_sampled_rows_match_full_evaluation():
+    """The sampled-row forms used at full sizes agree with whole-head evaluation."""
+    rng = _rng(14)
+    for causal in (False, True):
+        q, k, v, do = _rand(rng, 37, 5), _rand(rng, 37, 5), _rand(rng, 37, 5), _rand(rng, 37, 5)
+        o, lse = oracle.head_forward(q, k, v, 0.4, causal)
+        dq, dk, dv = oracle.head_backward(q, k, v, do, 0.4, causal)
+        rows = [0, 5, 17, 36]
+        o2, l2 = oracle.head_forward_rows(q, k, v, 0.4, causal, rows)
+        assert np.max(np.abs(o2 - o[rows])) < 1e-12 and np.max(np.abs(l2 - lse[rows])) < 1e-12
+        krows = [1, 9, 36]
+        dq2, dk2, dv2 = oracle.head_backward_rows(q, k, v, do, 0.4, causal, rows, krows,
+                                                  row_block=8)
+        assert np.max(np.abs(dq2 - dq[rows])) < 1e-12
+        assert np.max(np.abs(dk2 - dk[krows])) < 1e-12
+        assert np.max(np.abs(dv2 - dv[krows])) < 1e-12
