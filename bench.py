@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=1,
                     help="heads of the workload the CPU oracle times (bounded sample)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy (for scaling HBM counters)")
     ap.add_argument("--sweep", default="",
                     help="optional path: also time the fp16 length sweep and write JSON lines there")
     return ap.parse_args()
@@ -93,6 +95,38 @@ def time_path(fa, torch, case, dev, steps, warmup):
     return wall, avg
 
 
+KERNEL_SYMBOL = {"fwd": "fwd_kernel", "bwd_pre": "bwd_pre_kernel", "bwd_dkdv": "dkdv_kernel",
+                 "bwd_dq": "dq_kernel"}
+
+
+def library_source_sha():
+    import glob
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(root, "exact_attention_88_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, scaled by the plain-copy calibration; None when the
+    counters were taken on a different version of the kernel sources."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != library_source_sha():
+        return None
+    k = rec.get("kernels", {}).get(KERNEL_SYMBOL[kernel])
+    return None if k is None else round(float(k["bytes"]))
+
+
 def cpu_baseline(case, x, heads):
     """The CPU oracle, as it stands, on `heads` heads of the same workload."""
     import numpy as np
@@ -128,6 +162,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        nbytes = 512 << 20
+        src = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 5}), flush=True)
+        return
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from exact_attention_88_amd import fa
     from exact_attention_88_amd import workloads as W
@@ -167,7 +210,8 @@ def main():
         "kernel_ms": {n: round(v, 4) for n, v in avg.items()},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": MFMA_PEAK_F16, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_PEAK_F16, 4), "traffic": None},
+                     "frac": round(achieved / MFMA_PEAK_F16, 4),
+                     "traffic": measured_traffic(dom)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, x, args.cpu_heads)
