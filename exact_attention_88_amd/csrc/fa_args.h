@@ -50,6 +50,11 @@ const TileCfg* fwd_tile(int dtype, int D, int id);
 int fwd_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s);
 
+// Tuned fp16 / head-dim-128 forward (fa_fwd_f16.hip).
+int fwd_fast_variants();
+TileCfg fwd_fast_cfg(int variant);
+hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int causal, hipStream_t s);
+
 int dkdv_tile_count(int dtype, int D);
 const TileCfg* dkdv_tile(int dtype, int D, int id);
 int dkdv_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal);

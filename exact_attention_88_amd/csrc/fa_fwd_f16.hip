@@ -1,0 +1,262 @@
+// Forward attention for fp16 with head dim 128 on gfx950: the tuned path.
+//
+// Same method as the generic forward kernel ("FlashAttention-2 from PyTorch to
+// Triton": online softmax over streamed K/V tiles, one program per query tile;
+// "Triton FlashAttention": exp2 on log2(e)-prescaled scores, causal block
+// skipping, one LSE float per row), laid out for CDNA4:
+//   * K and V tiles are double-buffered in LDS: the global loads of tile t+1
+//     are issued into registers before tile t is computed and written to the
+//     other buffer afterwards, so one barrier per tile suffices and HBM/L2
+//     latency hides behind the MFMA work;
+//   * each tile is read in one pattern only, so each gets the row padding
+//     that makes that pattern bank-conflict free with plain base+offset
+//     addressing: K rows (read row-wise, 16 rows x one 16-byte chunk per
+//     ds_read_b128) are padded by 16 bytes, V rows (read transposed, 4 rows x
+//     64 bytes per ds_read_b64_tr_b16 half-wave) by 64 bytes;
+//   * the accumulator rescale is skipped when no row of the wave moved its max;
+//   * workgroups are renumbered so that all query blocks of one (batch, head)
+//     run on the same XCD (dispatch is round-robin over the 8 XCDs), letting
+//     that XCD's L2 serve the shared K/V stream; causal blocks run longest
+//     first.
+#include "fa_args.h"
+#include "fa_common.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kD = 128;
+
+constexpr int kLSK = kD + 8;   // K tile row stride (halfs): 272 bytes
+constexpr int kLSV = kD + 32;  // V tile row stride (halfs): 320 bytes
+
+// Map the hardware workgroup id to (query block, batch*head) so that
+// consecutive logical blocks share an XCD.
+__device__ __forceinline__ int xcd_logical_block() {
+  const int n = gridDim.x, id = blockIdx.x;
+  if (n % 8 != 0) return id;
+  return (id % 8) * (n / 8) + id / 8;
+}
+
+// Global -> register staging of a ROWS x 128 fp16 tile (16-byte chunks,
+// PER per thread) and register -> padded LDS store.  Native vector types keep
+// the staging in VGPRs.
+template <int ROWS, int NT>
+__device__ __forceinline__ void tile_load(u32x4* r, const half_t* __restrict__ base, int64_t ss,
+                                          int row0, int nrows) {
+  constexpr int PER = ROWS * 16 / NT;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = i * NT + (int)threadIdx.x;
+    const int row = min(row0 + (c >> 4), nrows - 1);  // rows past the end are masked later
+    r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * ss + ((c & 15) << 3));
+  }
+}
+
+template <int ROWS, int NT, int LS>
+__device__ __forceinline__ void tile_store(const u32x4* r, half_t* lds) {
+  constexpr int PER = ROWS * 16 / NT;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = i * NT + (int)threadIdx.x;
+    *reinterpret_cast<u32x4*>(lds + (c >> 4) * LS + ((c & 15) << 3)) = r[i];
+  }
+}
+
+// Row-wise operand fragment of the K tile: lane (c, g) gets row rbase + c,
+// chunk kchunk + g.
+__device__ __forceinline__ h8 frag_rows_k(const half_t* lds, int rbase, int kchunk) {
+  const int lane = threadIdx.x & 63;
+  return *reinterpret_cast<const h8*>(lds + (rbase + (lane & 31)) * kLSK +
+                                      (kchunk + (lane >> 5)) * 8);
+}
+
+// Transposed operand fragment (see frag_tr in fa_common.h) of the V tile.
+__device__ __forceinline__ h8 frag_tr_v(const half_t* lds, int rbase, int t, int cbase) {
+  const int lane = threadIdx.x & 63, g = lane >> 5, j = lane & 15;
+  const int col = cbase + ((lane >> 4) & 1) * 16 + (j & 3) * 4;
+  const int row = rbase + t * 16 + g * 4 + (j >> 2);
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const half_t* p0 = lds + row * kLSV + col;
+  s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
+  s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + 8 * kLSV));
+  h4 ah = __builtin_bit_cast(h4, a), bh = __builtin_bit_cast(h4, b);
+  h8 r;
+  r[0] = ah[0]; r[1] = ah[1]; r[2] = ah[2]; r[3] = ah[3];
+  r[4] = bh[0]; r[5] = bh[1]; r[6] = bh[2]; r[7] = bh[3];
+  return r;
+}
+
+template <int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
+  constexpr int BM = 32 * NW, NT = NW * 64;
+  constexpr int NKB = BN / 32;
+  constexpr int TK = BN * kLSK, TV = BN * kLSV;
+  __shared__ __attribute__((aligned(1024))) half_t smem[2 * TK + 2 * TV];  // K0 K1 V0 V1
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
+  const int nqb = (a.Sq + BM - 1) / BM;
+  const int L = xcd_logical_block();
+  int qb = L % nqb;
+  const int bh = L / nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+  const int b = bh / a.H, h = bh % a.H;
+  const half_t* qbase = (const half_t*)a.q.p + b * a.q.sb + h * a.q.sh;
+  const half_t* kbase = (const half_t*)a.k.p + b * a.k.sb + h * a.k.sh;
+  const half_t* vbase = (const half_t*)a.v.p + b * a.v.sb + h * a.v.sh;
+
+  const int q0 = qb * BM, qw = q0 + w * 32, qi = qw + c;
+
+  h8 qf[8];
+  {
+    const half_t* qrow = qbase + (int64_t)min(qi, a.Sq - 1) * a.q.ss;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const h8*>(qrow + ks * 16 + g * 8);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): Q is resident before the tile loop
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = zero16();
+  float m = -INFINITY, lsum = 0.f;
+  const float cs = a.scale_log2;
+
+  const int kend = CAUSAL ? min(a.Sk, q0 + BM) : a.Sk;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  constexpr int PER = BN * 16 / NT;
+  u32x4 kr[PER], vr[PER];
+  tile_load<BN, NT>(kr, kbase, a.k.ss, 0, a.Sk);
+  tile_load<BN, NT>(vr, vbase, a.v.ss, 0, a.Sk);
+  tile_store<BN, NT, kLSK>(kr, smem);
+  tile_store<BN, NT, kLSV>(vr, smem + 2 * TK);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    const int buf = t & 1;
+    const half_t* Ks = smem + buf * TK;
+    const half_t* Vs = smem + 2 * TK + buf * TV;
+    __syncthreads();
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      tile_load<BN, NT>(kr, kbase, a.k.ss, k0 + BN, a.Sk);
+      tile_load<BN, NT>(vr, vbase, a.v.ss, k0 + BN, a.Sk);
+    }
+    if (!(CAUSAL && k0 > qw + 31)) {
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        h8 kf[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) kf[ks] = frag_rows_k(Ks, kb * 32, ks * 2);
+        s[kb] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], s[kb], 0, 0, 0);
+      }
+      if ((k0 + BN > a.Sk) || (CAUSAL && k0 + BN - 1 > qw)) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + crow(r, g);
+            if (key >= a.Sk || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, xor32(mx));
+      const float mnew = fmaxf(m, mx);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float mc = muse * cs;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][r], cs, -mc));
+          s[kb][r] = p;
+          rs += p;
+        }
+      if (__any(mnew != m)) {
+        const float alpha = fast_exp2((m - muse) * cs);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      lsum += rs;
+      m = mnew;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          h8 vf[4];
+#pragma unroll
+          for (int db = 0; db < 4; ++db) vf[db] = frag_tr_v(Vs, kb * 32, tt, db * 32);
+          h8 pf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[e] = (half_t)s[kb][tt * 8 + e];
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pf, oacc[db], 0, 0, 0);
+        }
+    }
+    if (more) {
+      tile_store<BN, NT, kLSK>(kr, smem + (buf ^ 1) * TK);
+      tile_store<BN, NT, kLSV>(vr, smem + 2 * TK + (buf ^ 1) * TV);
+    }
+  }
+
+  const float ltot = lsum + xor32(lsum);
+  if (qi < a.Sq) {
+    const float inv = 1.f / ltot;
+    half_t* orow = (half_t*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        h4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (half_t)(oacc[db][r4 * 4 + e] * inv);
+        *reinterpret_cast<h4*>(orow + db * 32 + r4 * 8 + g * 4) = o4;
+      }
+    if (g == 0)
+      a.lse[(int64_t)bh * a.Sq + qi] = __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2);
+  }
+}
+
+template <int BN, int NW, bool CAUSAL>
+hipError_t launch(const FwdArgs& a, hipStream_t s) {
+  constexpr int BM = 32 * NW;
+  const int64_t grid = (((int64_t)a.Sq + BM - 1) / BM) * a.B * a.H;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_f16_d128<BN, NW, CAUSAL>),
+                         dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
+}
+
+}  // namespace
+
+// Variants: 0 = (BN 64, 4 waves), 1 = (BN 64, 8 waves), 2 = (BN 128, 4 waves).
+int fwd_fast_variants() { return 3; }
+
+TileCfg fwd_fast_cfg(int v) {
+  const int bn = v == 2 ? 128 : 64, nw = v == 1 ? 8 : 4;
+  return TileCfg{32 * nw, bn, nw, 2 * bn * (kLSK + kLSV) * 2};
+}
+
+hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int causal, hipStream_t s) {
+  switch (variant) {
+    case 0: return causal ? launch<64, 4, true>(a, s) : launch<64, 4, false>(a, s);
+    case 1: return causal ? launch<64, 8, true>(a, s) : launch<64, 8, false>(a, s);
+    case 2: return causal ? launch<128, 4, true>(a, s) : launch<128, 4, false>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa
