@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1,
+    ap.add_argument("--cpu-heads", type=int, default=3,
                     help="heads of the workload the CPU oracle times (bounded sample)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (for scaling HBM counters)")

@@ -67,4 +67,12 @@ hipError_t launch_dq(const BwdArgs& a, int dtype, int D, int causal, int tile, h
 
 hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int D, hipStream_t s);
 
+// Tuned fp16 / head-dim-128 backward kernels (fa_bwd_f16.hip).
+int dq_fast_variants();
+TileCfg dq_fast_cfg(int variant);
+hipError_t launch_dq_fast(const BwdArgs& a, int variant, int causal, hipStream_t s);
+int dkdv_fast_variants();
+TileCfg dkdv_fast_cfg(int variant);
+hipError_t launch_dkdv_fast(const BwdArgs& a, int variant, int causal, hipStream_t s);
+
 }  // namespace fa

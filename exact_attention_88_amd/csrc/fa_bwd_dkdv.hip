@@ -262,7 +262,11 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int dkdv_tile_count(int dtype, int D) {
+// fp16 with head dim 128 puts the tuned kernel's variants (fa_bwd_f16.hip)
+// first in its table; the generic entries follow.
+static int fast_count(int dtype, int D) { return (dtype == 0 && D == 128) ? dkdv_fast_variants() : 0; }
+
+static int generic_count(int dtype, int D) {
   switch (D) {
     case 16: return count_ok(dtype, 16);
     case 32: return count_ok(dtype, 32);
@@ -272,9 +276,17 @@ int dkdv_tile_count(int dtype, int D) {
   return 0;
 }
 
+int dkdv_tile_count(int dtype, int D) { return fast_count(dtype, D) + generic_count(dtype, D); }
+
 const TileCfg* dkdv_tile(int dtype, int D, int id) {
   static thread_local TileCfg cfg;
   if (id < 0 || id >= dkdv_tile_count(dtype, D)) return nullptr;
+  const int nf = fast_count(dtype, D);
+  if (id < nf) {
+    cfg = dkdv_fast_cfg(id);
+    return &cfg;
+  }
+  id -= nf;
   const Tile t = tile_at(dtype, raw_for(dtype, D, id));
   cfg = TileCfg{t.bm, 32 * t.nw, t.nw, lds_bytes(dtype == 0 ? 2 : 4, D, t.bm)};
   return &cfg;
@@ -286,7 +298,15 @@ int dkdv_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
 }
 
 hipError_t launch_dkdv(const BwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s) {
-  const int raw = raw_for(dtype, D, tile);
+  const int nf = fast_count(dtype, D);
+  if (tile < nf) {
+    // The tuned kernel needs 16-byte vector access to every tensor it touches;
+    // other layouts run the generic kernel's first entry instead.
+    const int need = VEC_Q | VEC_K | VEC_V | VEC_DO | VEC_DK | VEC_DV;
+    if ((a.vec & need) == need) return launch_dkdv_fast(a, tile, causal, s);
+    tile = nf;
+  }
+  const int raw = raw_for(dtype, D, tile - nf);
   if (raw < 0) return hipErrorInvalidValue;
   if (dtype == 0) {
     switch (D) {

@@ -189,7 +189,11 @@ int raw_for(int dtype, int D, int id) {
 
 }  // namespace
 
-int dq_tile_count(int dtype, int D) {
+// fp16 with head dim 128 puts the tuned kernel's variants (fa_bwd_f16.hip)
+// first in its table; the generic entries follow.
+static int fast_count(int dtype, int D) { return (dtype == 0 && D == 128) ? dq_fast_variants() : 0; }
+
+static int generic_count(int dtype, int D) {
   switch (D) {
     case 16: return count_ok(dtype, 16);
     case 32: return count_ok(dtype, 32);
@@ -199,9 +203,17 @@ int dq_tile_count(int dtype, int D) {
   return 0;
 }
 
+int dq_tile_count(int dtype, int D) { return fast_count(dtype, D) + generic_count(dtype, D); }
+
 const TileCfg* dq_tile(int dtype, int D, int id) {
   static thread_local TileCfg cfg;
   if (id < 0 || id >= dq_tile_count(dtype, D)) return nullptr;
+  const int nf = fast_count(dtype, D);
+  if (id < nf) {
+    cfg = dq_fast_cfg(id);
+    return &cfg;
+  }
+  id -= nf;
   const Tile t = tile_at(dtype, raw_for(dtype, D, id));
   cfg = TileCfg{32 * t.nw, t.bn, t.nw, lds_bytes(dtype == 0 ? 2 : 4, D, t.bn)};
   return &cfg;
@@ -213,7 +225,15 @@ int dq_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
 }
 
 hipError_t launch_dq(const BwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s) {
-  const int raw = raw_for(dtype, D, tile);
+  const int nf = fast_count(dtype, D);
+  if (tile < nf) {
+    // The tuned kernel needs 16-byte vector access to every tensor it touches;
+    // other layouts run the generic kernel's first entry instead.
+    const int need = VEC_Q | VEC_K | VEC_V | VEC_DO | VEC_DQ;
+    if ((a.vec & need) == need) return launch_dq_fast(a, tile, causal, s);
+    tile = nf;
+  }
+  const int raw = raw_for(dtype, D, tile - nf);
   if (raw < 0) return hipErrorInvalidValue;
   if (dtype == 0) {
     switch (D) {
