@@ -170,39 +170,39 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
     for (int kb = 0; kb < NKB; ++kb) {
       const int ks0 = k0 + kb * 32;
       if (CAUSAL && ks0 > qw + 31) continue;
+      // Row-wise operands of S^T and dP^T first, then the transposed K operand
+      // of dQ, so LDS latency overlaps the MFMAs and the softmax-gradient VALU.
+      h8 kf[8], vf[8], kt[2][4];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kf[ks] = frag_r(Kr, kb * 32, ks * 2);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) vf[ks] = frag_r(Vr, kb * 32, ks * 2);
       f32x16 s = zero16(), dp = zero16();
-      {
-        h8 kf[8];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) kf[ks] = frag_r(Kr, kb * 32, ks * 2);
+      for (int ks = 0; ks < 8; ++ks) s = mma(kf[ks], qf[ks], s);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) s = mma(kf[ks], qf[ks], s);
-      }
-      {
-        h8 vf[8];
+      for (int ks = 0; ks < 8; ++ks) dp = mma(vf[ks], df[ks], dp);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) vf[ks] = frag_r(Vr, kb * 32, ks * 2);
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) dp = mma(vf[ks], df[ks], dp);
-      }
-      const bool need_mask = (ks0 + 32 > a.Sk) || (CAUSAL && ks0 + 31 > qw);
+        for (int db = 0; db < 4; ++db) kt[tt][db] = frag_t(Kt, kb * 32, tt, db * 32);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[r], cs, -lse2));
-        if (need_mask) {
+      for (int r = 0; r < 16; ++r) s[r] = fast_exp2(__builtin_fmaf(s[r], cs, -lse2));
+      // Masks only on the diagonal block and the ragged key tail.
+      if ((ks0 + 32 > a.Sk) || (CAUSAL && ks0 + 31 > qw)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
           const int key = ks0 + crow(r, g);
-          if (key >= a.Sk || (CAUSAL && key > qi)) p = 0.f;
+          if (key >= a.Sk || (CAUSAL && key > qi)) s[r] = 0.f;
         }
-        s[r] = p * (dp[r] - dlt);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - dlt);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        h8 kt[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) kt[db] = frag_t(Kt, kb * 32, tt, db * 32);
         const h8 sf = cvt8(s, tt);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dq[db] = mma(kt[db], sf, dq[db]);
+        for (int db = 0; db < 4; ++db) dq[db] = mma(kt[tt][db], sf, dq[db]);
       }
     }
     if (more) {
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   constexpr int TR = BM * kLSR, TT = BM * kLST;
   constexpr int BUF = 2 * TR + 2 * TT;  // Q rows, dO rows, Q transposed, dO transposed
   __shared__ __attribute__((aligned(1024))) half_t smem[2 * BUF];
-  __shared__ float lsd[2][2][BM];  // [buffer][LSE*log2e, delta][row]
+  __shared__ __attribute__((aligned(16))) float lsd[2][2][BM];  // [buffer][LSE*log2e, delta][row]
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nkb = (a.Sk + BN - 1) / BN;
@@ -305,49 +305,62 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
     for (int qb = 0; qb < NQB; ++qb) {
       const int qs = q0 + qb * 32;
       if (CAUSAL && qs + 31 < kw) continue;  // every query of the block precedes every key
-      f32x16 s = zero16();
-      {
-        h8 qf[8];
+      // Row-wise operands first (S and dP do not depend on each other), then the
+      // transposed operands of dV and dK, so LDS latency overlaps the MFMAs.
+      h8 qf[8], of[8];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r(Qr, qb * 32, ks * 2);
+      for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r(Qr, qb * 32, ks * 2);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) s = mma(qf[ks], kf[ks], s);
+      for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r(Dr, qb * 32, ks * 2);
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) s = mma(qf[ks], kf[ks], s);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) dp = mma(of[ks], vf[ks], dp);
+      h8 dt[2][4], qt[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dt[tt][db] = frag_t(Dt, qb * 32, tt, db * 32);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) qt[tt][db] = frag_t(Qt, qb * 32, tt, db * 32);
+      // Per-row LSE and delta for the accumulator rows crow(r, g): 4 runs of 4.
+      float4 l4[4], d4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        l4[i] = *reinterpret_cast<const float4*>(Ls + qb * 32 + i * 8 + g * 4);
+        d4[i] = *reinterpret_cast<const float4*>(Dl + qb * 32 + i * 8 + g * 4);
       }
-      const bool need_mask = key_tail || (CAUSAL && qs < kw + 31);
+      f32x16 p, ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qr_ = qb * 32 + crow(r, g);
-        float p = fast_exp2(__builtin_fmaf(s[r], cs, -Ls[qr_]));
-        if (need_mask && (kj >= a.Sk || (CAUSAL && kj > q0 + qr_))) p = 0.f;
-        s[r] = p;
+        const float lr = r % 4 == 0 ? l4[r / 4].x : r % 4 == 1 ? l4[r / 4].y : r % 4 == 2 ? l4[r / 4].z : l4[r / 4].w;
+        p[r] = fast_exp2(__builtin_fmaf(s[r], cs, -lr));
+      }
+      // Masks only on the diagonal block and the ragged key tail.
+      if (key_tail || (CAUSAL && qs < kw + 31)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kj >= a.Sk || (CAUSAL && kj > qs + crow(r, g))) p[r] = 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float dr = r % 4 == 0 ? d4[r / 4].x : r % 4 == 1 ? d4[r / 4].y : r % 4 == 2 ? d4[r / 4].z : d4[r / 4].w;
+        ds[r] = p[r] * (dp[r] - dr);
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        h8 dt[4];
+        const h8 pf = cvt8(p, tt);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dt[db] = frag_t(Dt, qb * 32, tt, db * 32);
-        const h8 pf = cvt8(s, tt);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dv[db] = mma(dt[db], pf, dv[db]);
+        for (int db = 0; db < 4; ++db) dv[db] = mma(dt[tt][db], pf, dv[db]);
       }
-      f32x16 dp = zero16();
-      {
-        h8 of[8];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r(Dr, qb * 32, ks * 2);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) dp = mma(of[ks], vf[ks], dp);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - Dl[qb * 32 + crow(r, g)]);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        h8 qt[4];
+        const h8 sf = cvt8(ds, tt);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) qt[db] = frag_t(Qt, qb * 32, tt, db * 32);
-        const h8 sf = cvt8(s, tt);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dk[db] = mma(qt[db], sf, dk[db]);
+        for (int db = 0; db < 4; ++db) dk[db] = mma(qt[tt][db], sf, dk[db]);
       }
     }
     if (more) store_rows(buf ^ 1);
@@ -398,7 +411,9 @@ hipError_t launch_dq_fast(const BwdArgs& a, int v, int causal, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// dK/dV variants: 0 = (BM 64, 4 waves), 1 = (BM 32, 4 waves).
+// dK/dV variants: 0 = (BM 64, 4 waves), 1 = (BM 32, 4 waves).  (With 8 waves,
+// two per SIMD, the 32 keys' K, V, dK and dV no longer fit the 256 registers
+// a wave then gets, and the compiler spills.)
 int dkdv_fast_variants() { return 2; }
 TileCfg dkdv_fast_cfg(int v) {
   const int bm = v == 1 ? 32 : 64, nw = 4;
