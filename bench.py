@@ -95,10 +95,6 @@ def time_path(fa, torch, case, dev, steps, warmup):
     return wall, avg
 
 
-KERNEL_SYMBOL = {"fwd": "fwd_kernel", "bwd_pre": "bwd_pre_kernel", "bwd_dkdv": "dkdv_kernel",
-                 "bwd_dq": "dq_kernel"}
-
-
 def library_source_sha():
     import glob
     import hashlib
@@ -123,7 +119,7 @@ def measured_traffic(kernel):
         return None
     if rec.get("source_sha") != library_source_sha():
         return None
-    k = rec.get("kernels", {}).get(KERNEL_SYMBOL[kernel])
+    k = rec.get("kernels", {}).get(kernel)
     return None if k is None else round(float(k["bytes"]))
 
 
