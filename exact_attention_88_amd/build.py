@@ -36,12 +36,37 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
+# Translation units holding the tuned kernels: any scratch (spilled or
+# stack-allocated) memory in them is a build error, since a spill inside their
+# tile loops costs more than the tuning gains.
+NO_SCRATCH = {"fa_fwd_f16.hip", "fa_bwd_f16.hip"}
+
+
+def _scratch_kernels(remarks: str):
+    """(kernel, bytes) for every kernel whose resource remark reports scratch."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line and name:
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split("[")[0].strip())
+            if size:
+                out.append((name, size))
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src in NO_SCRATCH:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if src in NO_SCRATCH:
+        bad = _scratch_kernels(res.stderr)
+        if bad:
+            raise RuntimeError(f"{src}: tuned kernels use scratch memory: {bad}")
     return obj
 
 

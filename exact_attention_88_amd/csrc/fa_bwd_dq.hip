@@ -220,7 +220,10 @@ const TileCfg* dq_tile(int dtype, int D, int id) {
 }
 
 int dq_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
-  (void)dtype; (void)D; (void)Sq; (void)Sk; (void)causal;
+  (void)Sq; (void)Sk; (void)causal;
+  // fp16, D = 128: the tuned kernel with 8 waves and 32-key tiles measured
+  // fastest on MI355X at S = 4096 and 16384, causal and not.
+  if (dtype == 0 && D == 128) return 2;
   return 0;
 }
 

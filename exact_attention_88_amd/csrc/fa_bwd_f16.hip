@@ -171,8 +171,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
       const int ks0 = k0 + kb * 32;
       if (CAUSAL && ks0 > qw + 31) continue;
       // Row-wise operands of S^T and dP^T first, then the transposed K operand
-      // of dQ, so LDS latency overlaps the MFMAs and the softmax-gradient VALU.
-      h8 kf[8], vf[8], kt[2][4];
+      // of dQ (one k-step at a time: with 8 waves a wave has 256 registers).
+      h8 kf[8], vf[8];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) kf[ks] = frag_r(Kr, kb * 32, ks * 2);
 #pragma unroll
@@ -182,10 +182,6 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
       for (int ks = 0; ks < 8; ++ks) s = mma(kf[ks], qf[ks], s);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) dp = mma(vf[ks], df[ks], dp);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) kt[tt][db] = frag_t(Kt, kb * 32, tt, db * 32);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = fast_exp2(__builtin_fmaf(s[r], cs, -lse2));
       // Masks only on the diagonal block and the ragged key tail.
@@ -200,9 +196,12 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
       for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - dlt);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
+        h8 kt[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) kt[db] = frag_t(Kt, kb * 32, tt, db * 32);
         const h8 sf = cvt8(s, tt);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dq[db] = mma(kt[tt][db], sf, dq[db]);
+        for (int db = 0; db < 4; ++db) dq[db] = mma(kt[db], sf, dq[db]);
       }
     }
     if (more) {

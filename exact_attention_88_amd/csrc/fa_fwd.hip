@@ -248,10 +248,11 @@ const TileCfg* fwd_tile(int dtype, int D, int id) {
 }
 
 int fwd_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
-  (void)Sq; (void)Sk; (void)causal;
-  // fp16, D = 128: the tuned kernel with 8 waves (256 query rows) and 64-key
-  // tiles measured fastest on MI355X at S = 4096 and 16384, causal and not.
-  if (dtype == 0 && D == 128) return 1;
+  // fp16, D = 128, by measurement on MI355X (S = 4096 and 16384): the
+  // software-pipelined 4-wave kernel for causal attention up to 4096 keys
+  // (twice the workgroups of the 8-wave one), the tuned 8-wave kernel
+  // otherwise (pipelined and plain 8-wave kernels measure the same there).
+  if (dtype == 0 && D == 128) return (causal && Sq <= 4096 && Sk <= 4096) ? 5 : 1;
   return 0;
 }
 

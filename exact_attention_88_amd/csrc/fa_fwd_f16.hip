@@ -230,6 +230,182 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
   }
 }
 
+// Scores of one tile for one wave: NKB 32x32 blocks S^T = K Q^T.
+template <int NKB>
+__device__ __forceinline__ void scores(f32x16* s, const half_t* Ks, const h8* qf) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    h8 kf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = frag_rows_k(Ks, kb * 32, ks * 2);
+    s[kb] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], s[kb], 0, 0, 0);
+    // All eight fragment reads in flight before the first MFMA of the block.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  }
+}
+
+// Software-pipelined variant: while the softmax of tile t runs on the VALU,
+// the scores of tile t+1 are computed on the MFMA pipe, so the two overlap
+// within each wave instead of alternating.  K therefore runs one tile ahead of
+// V through LDS: iteration t loads K(t+2) and V(t+1) from HBM, computes
+// S(t+1) from K(t+1), softmax(t), then O += P(t) V(t), and stores the staged
+// tiles into the buffers that held K(t) and V(t-1).  One barrier per tile.
+template <int BN, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pp(FwdArgs a) {
+  constexpr int BM = 32 * NW, NT = NW * 64;
+  constexpr int NKB = BN / 32;
+  constexpr int TK = BN * kLSK, TV = BN * kLSV;
+  __shared__ __attribute__((aligned(1024))) half_t smem[2 * TK + 2 * TV];  // K0 K1 V0 V1
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
+  const int nqb = (a.Sq + BM - 1) / BM;
+  const int L = xcd_logical_block();
+  int qb = L % nqb;
+  const int bh = L / nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+  const int b = bh / a.H, h = bh % a.H;
+  const half_t* qbase = (const half_t*)a.q.p + b * a.q.sb + h * a.q.sh;
+  const half_t* kbase = (const half_t*)a.k.p + b * a.k.sb + h * a.k.sh;
+  const half_t* vbase = (const half_t*)a.v.p + b * a.v.sb + h * a.v.sh;
+
+  const int q0 = qb * BM, qw = q0 + w * 32, qi = qw + c;
+
+  h8 qf[8];
+  {
+    const half_t* qrow = qbase + (int64_t)min(qi, a.Sq - 1) * a.q.ss;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const h8*>(qrow + ks * 16 + g * 8);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): Q is resident before the tile loop
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = zero16();
+  float m = -INFINITY, lsum = 0.f;
+  const float cs = a.scale_log2;
+
+  const int kend = CAUSAL ? min(a.Sk, q0 + BM) : a.Sk;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  constexpr int PER = BN * 16 / NT;
+  u32x4 kr[PER], vr[PER];
+  tile_load<BN, NT>(kr, kbase, a.k.ss, 0, a.Sk);
+  tile_load<BN, NT>(vr, vbase, a.v.ss, 0, a.Sk);
+  tile_store<BN, NT, kLSK>(kr, smem);
+  tile_store<BN, NT, kLSV>(vr, smem + 2 * TK);
+  if (ntiles > 1) {
+    tile_load<BN, NT>(kr, kbase, a.k.ss, BN, a.Sk);
+    tile_store<BN, NT, kLSK>(kr, smem + TK);
+  }
+  __syncthreads();
+  f32x16 scur[NKB];
+  scores<NKB>(scur, smem, qf);
+
+  // Every wave runs every tile of its block: a tile entirely after a wave's
+  // rows is fully masked (P = 0) and changes nothing, and keeping the work
+  // unconditional keeps S(t+1) and softmax(t) in one basic block, where the
+  // scheduler can interleave MFMA and VALU.  In the last iteration S(t+1)
+  // reads a stale K buffer and is discarded.
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    const bool more1 = t + 1 < ntiles, more2 = t + 2 < ntiles;
+    if (more2) tile_load<BN, NT>(kr, kbase, a.k.ss, k0 + 2 * BN, a.Sk);
+    if (more1) tile_load<BN, NT>(vr, vbase, a.v.ss, k0 + BN, a.Sk);
+    {
+      if ((k0 + BN > a.Sk) || (CAUSAL && k0 + BN - 1 > qw)) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + crow(r, g);
+            if (key >= a.Sk || (CAUSAL && key > qi)) scur[kb][r] = -INFINITY;
+          }
+      }
+      f32x16 snxt[NKB];
+      scores<NKB>(snxt, smem + ((t + 1) & 1) * TK, qf);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb][r]);
+      mx = fmaxf(mx, xor32(mx));
+      const float mnew = fmaxf(m, mx);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float mc = muse * cs;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(scur[kb][r], cs, -mc));
+          scur[kb][r] = p;
+          rs += p;
+        }
+      if (__any(mnew != m)) {
+        const float alpha = fast_exp2((m - muse) * cs);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      lsum += rs;
+      m = mnew;
+      const half_t* Vs = smem + 2 * TK + (t & 1) * TV;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          h8 vf[4];
+#pragma unroll
+          for (int db = 0; db < 4; ++db) vf[db] = frag_tr_v(Vs, kb * 32, tt, db * 32);
+          h8 pf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[e] = (half_t)scur[kb][tt * 8 + e];
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pf, oacc[db], 0, 0, 0);
+        }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) scur[kb] = snxt[kb];
+    }
+    if (more2) tile_store<BN, NT, kLSK>(kr, smem + (t & 1) * TK);
+    if (more1) tile_store<BN, NT, kLSV>(vr, smem + 2 * TK + ((t + 1) & 1) * TV);
+    __syncthreads();
+  }
+
+  const float ltot = lsum + xor32(lsum);
+  if (qi < a.Sq) {
+    const float inv = 1.f / ltot;
+    half_t* orow = (half_t*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        h4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (half_t)(oacc[db][r4 * 4 + e] * inv);
+        *reinterpret_cast<h4*>(orow + db * 32 + r4 * 8 + g * 4) = o4;
+      }
+    if (g == 0)
+      a.lse[(int64_t)bh * a.Sq + qi] = __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2);
+  }
+}
+
+template <int BN, int NW, bool CAUSAL>
+hipError_t launch_pp(const FwdArgs& a, hipStream_t s) {
+  constexpr int BM = 32 * NW;
+  const int64_t grid = (((int64_t)a.Sq + BM - 1) / BM) * a.B * a.H;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_f16_d128_pp<BN, NW, CAUSAL>),
+                         dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
+}
+
 template <int BN, int NW, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
   constexpr int BM = 32 * NW;
@@ -242,11 +418,13 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Variants: 0 = (BN 64, 4 waves), 1 = (BN 64, 8 waves), 2 = (BN 128, 4 waves).
-int fwd_fast_variants() { return 3; }
+// Variants: 0 = (BN 64, 4 waves), 1 = (BN 64, 8 waves), 2 = (BN 128, 4 waves);
+// software-pipelined: 3 = (BN 64, 8 waves), 4 = (BN 32, 8 waves), 5 = (BN 64, 4 waves).
+int fwd_fast_variants() { return 6; }
 
 TileCfg fwd_fast_cfg(int v) {
-  const int bn = v == 2 ? 128 : 64, nw = v == 1 ? 8 : 4;
+  const int bn = v == 2 ? 128 : v == 4 ? 32 : 64;
+  const int nw = (v == 1 || v == 3 || v == 4) ? 8 : 4;
   return TileCfg{32 * nw, bn, nw, 2 * bn * (kLSK + kLSV) * 2};
 }
 
@@ -255,6 +433,9 @@ hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int causal, hipStream_
     case 0: return causal ? launch<64, 4, true>(a, s) : launch<64, 4, false>(a, s);
     case 1: return causal ? launch<64, 8, true>(a, s) : launch<64, 8, false>(a, s);
     case 2: return causal ? launch<128, 4, true>(a, s) : launch<128, 4, false>(a, s);
+    case 3: return causal ? launch_pp<64, 8, true>(a, s) : launch_pp<64, 8, false>(a, s);
+    case 4: return causal ? launch_pp<32, 8, true>(a, s) : launch_pp<32, 8, false>(a, s);
+    case 5: return causal ? launch_pp<64, 4, true>(a, s) : launch_pp<64, 4, false>(a, s);
   }
   return hipErrorInvalidValue;
 }
