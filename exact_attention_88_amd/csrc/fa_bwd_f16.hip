@@ -10,10 +10,12 @@
 //     global loads of tile t+1 are issued before tile t is computed), one
 //     barrier per tile;
 //   * a tile read both row-wise (as an untransposed MFMA operand) and
-//     transposed (ds_read_b64_tr_b16) is stored twice, once with the 16-byte
-//     row padding that makes 16-row ds_read_b128 reads conflict free and once
-//     with the 64-byte padding that makes 4-row transposed reads conflict
-//     free, so every fragment address is a base plus an immediate;
+//     transposed (ds_read_b64_tr_b16) is either stored once in an XOR-swizzled
+//     unpadded layout that is conflict free for both read patterns (the
+//     default variants: half the LDS stores and footprint), or twice, once
+//     with the 16-byte row padding that makes 16-row ds_read_b128 reads
+//     conflict free and once with the 64-byte padding that makes 4-row
+//     transposed reads conflict free;
 //   * all blocks of one (batch, head) are renumbered onto one XCD.
 // dQ kernel: one workgroup per 32*waves query rows; Q, dO, LSE and delta of
 // the wave's 32 rows live in registers, K and V stream (K in both layouts).
@@ -81,6 +83,49 @@ __device__ __forceinline__ h8 frag_t(const half_t* lds, int rbase, int t, int cb
   return r;
 }
 
+// Single-copy swizzled layout: unpadded 256-byte rows in which the 16-byte
+// chunk k of row r sits at chunk position k ^ swz(r).  swz(r) takes distinct
+// values on any 16 consecutive rows (so 16-row ds_read_b128 row reads and
+// full-row stores are conflict free) and, on 4 rows that start at a multiple
+// of 4, spreads 4 neighbouring chunks over all 16 chunk positions (so 4-row
+// transposed reads are conflict free).  One layout serves both read patterns.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+template <int ROWS, int NT>
+__device__ __forceinline__ void tile_store_swz(const u32x4* r, half_t* lds) {
+  constexpr int PER = ROWS * 16 / NT;
+  static_assert(NT % 256 == 0, "every thread keeps its row residue mod 16");
+  const int row0 = (int)threadIdx.x >> 4, off = row0 * kD + (((threadIdx.x & 15) ^ swz(row0)) << 3);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) *reinterpret_cast<u32x4*>(lds + i * (NT / 16) * kD + off) = r[i];
+}
+
+// Row-wise fragment in the swizzled layout; rbase is a multiple of 16.
+__device__ __forceinline__ h8 frag_r_swz(const half_t* lds, int rbase, int kchunk) {
+  const int lane = threadIdx.x & 63, r = lane & 31;
+  return *reinterpret_cast<const h8*>(lds + (rbase + r) * kD +
+                                      (((kchunk + (lane >> 5)) ^ swz(r)) << 3));
+}
+
+// Transposed fragment in the swizzled layout (same lanes as frag_t); rbase is
+// a multiple of 16 and cbase of 8.
+__device__ __forceinline__ h8 frag_t_swz(const half_t* lds, int rbase, int t, int cbase) {
+  const int lane = threadIdx.x & 63, g = lane >> 5, j = lane & 15;
+  const int col = ((lane >> 4) & 1) * 16 + (j & 3) * 4;
+  const int r = g * 4 + (j >> 2);
+  const int ch = (cbase >> 3) + (col >> 3);
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const half_t* p0 = lds + (rbase + t * 16 + r) * kD + ((ch ^ swz(r)) << 3) + (col & 7);
+  const half_t* p1 = lds + (rbase + t * 16 + r + 8) * kD + ((ch ^ swz(r + 8)) << 3) + (col & 7);
+  s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
+  s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1));
+  h4 ah = __builtin_bit_cast(h4, a), bh = __builtin_bit_cast(h4, b);
+  h8 x;
+  x[0] = ah[0]; x[1] = ah[1]; x[2] = ah[2]; x[3] = ah[3];
+  x[4] = bh[0]; x[5] = bh[1]; x[6] = bh[2]; x[7] = bh[3];
+  return x;
+}
+
 __device__ __forceinline__ f32x16 mma(h8 a, h8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -105,11 +150,13 @@ __device__ __forceinline__ void store_row4x4(half_t* rowp, const f32x16* acc, fl
 }
 
 // ------------------------------------------------------------------- dQ
-template <int BN, int NW, bool CAUSAL>
+// SWZ: K and V are stored once each in the swizzled layout (K serves both its
+// row-wise and its transposed reads) instead of K twice in the padded layouts.
+template <int BN, int NW, bool CAUSAL, bool SWZ>
 __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
   constexpr int BM = 32 * NW, NT = NW * 64, NKB = BN / 32;
-  constexpr int TR = BN * kLSR, TT = BN * kLST;
-  constexpr int BUF = 2 * TR + TT;  // K rows, V rows, K transposed
+  constexpr int TR = SWZ ? BN * kD : BN * kLSR, TT = SWZ ? 0 : BN * kLST;
+  constexpr int BUF = 2 * TR + TT;  // K rows, V rows[, K transposed]
   __shared__ __attribute__((aligned(1024))) half_t smem[2 * BUF];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
@@ -151,15 +198,23 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
   u32x4 kr[PER], vr[PER];
   tile_load<BN, NT>(kr, kbase, a.k.ss, 0, a.Sk);
   tile_load<BN, NT>(vr, vbase, a.v.ss, 0, a.Sk);
-  tile_store<BN, NT, kLSR>(kr, smem);
-  tile_store<BN, NT, kLSR>(vr, smem + TR);
-  tile_store<BN, NT, kLST>(kr, smem + 2 * TR);
+  auto store_tiles = [&](half_t* nb) {
+    if constexpr (SWZ) {
+      tile_store_swz<BN, NT>(kr, nb);
+      tile_store_swz<BN, NT>(vr, nb + TR);
+    } else {
+      tile_store<BN, NT, kLSR>(kr, nb);
+      tile_store<BN, NT, kLSR>(vr, nb + TR);
+      tile_store<BN, NT, kLST>(kr, nb + 2 * TR);
+    }
+  };
+  store_tiles(smem);
 
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BN;
     const half_t* Kr = smem + (t & 1) * BUF;
     const half_t* Vr = Kr + TR;
-    const half_t* Kt = Kr + 2 * TR;
+    const half_t* Kt = SWZ ? Kr : Kr + 2 * TR;
     __syncthreads();
     const bool more = t + 1 < ntiles;
     if (more) {
@@ -174,9 +229,11 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
       // of dQ (one k-step at a time: with 8 waves a wave has 256 registers).
       h8 kf[8], vf[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) kf[ks] = frag_r(Kr, kb * 32, ks * 2);
+      for (int ks = 0; ks < 8; ++ks)
+        kf[ks] = SWZ ? frag_r_swz(Kr, kb * 32, ks * 2) : frag_r(Kr, kb * 32, ks * 2);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) vf[ks] = frag_r(Vr, kb * 32, ks * 2);
+      for (int ks = 0; ks < 8; ++ks)
+        vf[ks] = SWZ ? frag_r_swz(Vr, kb * 32, ks * 2) : frag_r(Vr, kb * 32, ks * 2);
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) s = mma(kf[ks], qf[ks], s);
@@ -198,18 +255,14 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
       for (int tt = 0; tt < 2; ++tt) {
         h8 kt[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) kt[db] = frag_t(Kt, kb * 32, tt, db * 32);
+        for (int db = 0; db < 4; ++db)
+          kt[db] = SWZ ? frag_t_swz(Kt, kb * 32, tt, db * 32) : frag_t(Kt, kb * 32, tt, db * 32);
         const h8 sf = cvt8(s, tt);
 #pragma unroll
         for (int db = 0; db < 4; ++db) dq[db] = mma(kt[db], sf, dq[db]);
       }
     }
-    if (more) {
-      half_t* nb = smem + ((t + 1) & 1) * BUF;
-      tile_store<BN, NT, kLSR>(kr, nb);
-      tile_store<BN, NT, kLSR>(vr, nb + TR);
-      tile_store<BN, NT, kLST>(kr, nb + 2 * TR);
-    }
+    if (more) store_tiles(smem + ((t + 1) & 1) * BUF);
   }
 
   if (valid) {
@@ -219,11 +272,13 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------- dK / dV
-template <int BM, int NW, bool CAUSAL>
+// SWZ: Q and dO are stored once each in the swizzled layout instead of twice
+// in the padded layouts.
+template <int BM, int NW, bool CAUSAL, bool SWZ>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   constexpr int BN = 32 * NW, NT = NW * 64, NQB = BM / 32;
-  constexpr int TR = BM * kLSR, TT = BM * kLST;
-  constexpr int BUF = 2 * TR + 2 * TT;  // Q rows, dO rows, Q transposed, dO transposed
+  constexpr int TR = SWZ ? BM * kD : BM * kLSR, TT = SWZ ? 0 : BM * kLST;
+  constexpr int BUF = 2 * TR + 2 * TT;  // Q rows, dO rows[, Q transposed, dO transposed]
   __shared__ __attribute__((aligned(1024))) half_t smem[2 * BUF];
   __shared__ __attribute__((aligned(16))) float lsd[2][2][BM];  // [buffer][LSE*log2e, delta][row]
 
@@ -274,10 +329,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   };
   auto store_rows = [&](int buf) {
     half_t* base = smem + buf * BUF;
-    tile_store<BM, NT, kLSR>(qr, base);
-    tile_store<BM, NT, kLSR>(dr, base + TR);
-    tile_store<BM, NT, kLST>(qr, base + 2 * TR);
-    tile_store<BM, NT, kLST>(dr, base + 2 * TR + TT);
+    if constexpr (SWZ) {
+      tile_store_swz<BM, NT>(qr, base);
+      tile_store_swz<BM, NT>(dr, base + TR);
+    } else {
+      tile_store<BM, NT, kLSR>(qr, base);
+      tile_store<BM, NT, kLSR>(dr, base + TR);
+      tile_store<BM, NT, kLST>(qr, base + 2 * TR);
+      tile_store<BM, NT, kLST>(dr, base + 2 * TR + TT);
+    }
     if ((int)threadIdx.x < BM) {
       lsd[buf][0][threadIdx.x] = lsr;
       lsd[buf][1][threadIdx.x] = dlr;
@@ -293,8 +353,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
     const int buf = t & 1;
     const half_t* Qr = smem + buf * BUF;
     const half_t* Dr = Qr + TR;
-    const half_t* Qt = Qr + 2 * TR;
-    const half_t* Dt = Qt + TT;
+    const half_t* Qt = SWZ ? Qr : Qr + 2 * TR;
+    const half_t* Dt = SWZ ? Dr : Qt + TT;
     const float* Ls = lsd[buf][0];
     const float* Dl = lsd[buf][1];
     __syncthreads();
@@ -308,9 +368,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
       // transposed operands of dV and dK, so LDS latency overlaps the MFMAs.
       h8 qf[8], of[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r(Qr, qb * 32, ks * 2);
+      for (int ks = 0; ks < 8; ++ks)
+        qf[ks] = SWZ ? frag_r_swz(Qr, qb * 32, ks * 2) : frag_r(Qr, qb * 32, ks * 2);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r(Dr, qb * 32, ks * 2);
+      for (int ks = 0; ks < 8; ++ks)
+        of[ks] = SWZ ? frag_r_swz(Dr, qb * 32, ks * 2) : frag_r(Dr, qb * 32, ks * 2);
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) s = mma(qf[ks], kf[ks], s);
@@ -320,11 +382,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dt[tt][db] = frag_t(Dt, qb * 32, tt, db * 32);
+        for (int db = 0; db < 4; ++db)
+          dt[tt][db] = SWZ ? frag_t_swz(Dt, qb * 32, tt, db * 32) : frag_t(Dt, qb * 32, tt, db * 32);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) qt[tt][db] = frag_t(Qt, qb * 32, tt, db * 32);
+        for (int db = 0; db < 4; ++db)
+          qt[tt][db] = SWZ ? frag_t_swz(Qt, qb * 32, tt, db * 32) : frag_t(Qt, qb * 32, tt, db * 32);
       // Per-row LSE and delta for the accumulator rows crow(r, g): 4 runs of 4.
       float4 l4[4], d4[4];
 #pragma unroll
@@ -373,55 +437,64 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   }
 }
 
-template <int BN, int NW, bool CAUSAL>
+template <int BN, int NW, bool CAUSAL, bool SWZ>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
   constexpr int BM = 32 * NW;
   const int64_t grid = (((int64_t)a.Sq + BM - 1) / BM) * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_f16_d128<BN, NW, CAUSAL>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_f16_d128<BN, NW, CAUSAL, SWZ>),
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
 }
 
-template <int BM, int NW, bool CAUSAL>
+template <int BM, int NW, bool CAUSAL, bool SWZ>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
   constexpr int BN = 32 * NW;
   const int64_t grid = (((int64_t)a.Sk + BN - 1) / BN) * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_f16_d128<BM, NW, CAUSAL>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_f16_d128<BM, NW, CAUSAL, SWZ>),
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
 }
 
 }  // namespace
 
-// dQ variants: 0 = (BN 64, 8 waves), 1 = (BN 64, 4 waves), 2 = (BN 32, 8 waves).
-int dq_fast_variants() { return 3; }
+// dQ variants: 0 = (BN 64, 8 waves), 1 = (BN 64, 4 waves), 2 = (BN 32, 8 waves);
+// 3, 4 = (BN 32, 64; 8 waves) with swizzled single-copy K and V.  (With
+// 128-key tiles the staging registers push the non-causal kernel into spills.)
+int dq_fast_variants() { return 5; }
 TileCfg dq_fast_cfg(int v) {
-  const int bn = v == 2 ? 32 : 64, nw = v == 1 ? 4 : 8;
-  return TileCfg{32 * nw, bn, nw, 2 * bn * (2 * kLSR + kLST) * 2};
+  const int bn = v == 2 || v == 3 ? 32 : 64, nw = v == 1 ? 4 : 8;
+  const int row_halfs = v >= 3 ? 2 * kD : 2 * kLSR + kLST;
+  return TileCfg{32 * nw, bn, nw, 2 * bn * row_halfs * 2};
 }
 hipError_t launch_dq_fast(const BwdArgs& a, int v, int causal, hipStream_t s) {
   switch (v) {
-    case 0: return causal ? launch_dq_t<64, 8, true>(a, s) : launch_dq_t<64, 8, false>(a, s);
-    case 1: return causal ? launch_dq_t<64, 4, true>(a, s) : launch_dq_t<64, 4, false>(a, s);
-    case 2: return causal ? launch_dq_t<32, 8, true>(a, s) : launch_dq_t<32, 8, false>(a, s);
+    case 0: return causal ? launch_dq_t<64, 8, true, false>(a, s) : launch_dq_t<64, 8, false, false>(a, s);
+    case 1: return causal ? launch_dq_t<64, 4, true, false>(a, s) : launch_dq_t<64, 4, false, false>(a, s);
+    case 2: return causal ? launch_dq_t<32, 8, true, false>(a, s) : launch_dq_t<32, 8, false, false>(a, s);
+    case 3: return causal ? launch_dq_t<32, 8, true, true>(a, s) : launch_dq_t<32, 8, false, true>(a, s);
+    case 4: return causal ? launch_dq_t<64, 8, true, true>(a, s) : launch_dq_t<64, 8, false, true>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
-// dK/dV variants: 0 = (BM 64, 4 waves), 1 = (BM 32, 4 waves).  (With 8 waves,
-// two per SIMD, the 32 keys' K, V, dK and dV no longer fit the 256 registers
-// a wave then gets, and the compiler spills.)
-int dkdv_fast_variants() { return 2; }
+// dK/dV variants: 0 = (BM 64, 4 waves), 1 = (BM 32, 4 waves), 2 = (BM 64,
+// 4 waves, swizzled single-copy Q and dO), 3 = (BM 128, 4 waves, swizzled).  (With 8 waves, two per SIMD, the
+// 32 keys' K, V, dK and dV no longer fit the 256 registers a wave then gets,
+// and the compiler spills.)
+int dkdv_fast_variants() { return 4; }
 TileCfg dkdv_fast_cfg(int v) {
-  const int bm = v == 1 ? 32 : 64, nw = 4;
-  return TileCfg{bm, 32 * nw, nw, 2 * bm * (2 * kLSR + 2 * kLST) * 2 + 2 * 2 * bm * 4};
+  const int bm = v == 1 ? 32 : v == 3 ? 128 : 64, nw = 4;
+  const int row_halfs = v >= 2 ? 2 * kD : 2 * kLSR + 2 * kLST;
+  return TileCfg{bm, 32 * nw, nw, 2 * bm * row_halfs * 2 + 2 * 2 * bm * 4};
 }
 hipError_t launch_dkdv_fast(const BwdArgs& a, int v, int causal, hipStream_t s) {
   switch (v) {
-    case 0: return causal ? launch_dkdv_t<64, 4, true>(a, s) : launch_dkdv_t<64, 4, false>(a, s);
-    case 1: return causal ? launch_dkdv_t<32, 4, true>(a, s) : launch_dkdv_t<32, 4, false>(a, s);
+    case 0: return causal ? launch_dkdv_t<64, 4, true, false>(a, s) : launch_dkdv_t<64, 4, false, false>(a, s);
+    case 1: return causal ? launch_dkdv_t<32, 4, true, false>(a, s) : launch_dkdv_t<32, 4, false, false>(a, s);
+    case 2: return causal ? launch_dkdv_t<64, 4, true, true>(a, s) : launch_dkdv_t<64, 4, false, true>(a, s);
+    case 3: return causal ? launch_dkdv_t<128, 4, true, true>(a, s) : launch_dkdv_t<128, 4, false, true>(a, s);
   }
   return hipErrorInvalidValue;
 }
