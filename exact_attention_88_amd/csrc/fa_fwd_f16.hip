@@ -13,11 +13,16 @@
 //     addressing: K rows (read row-wise, 16 rows x one 16-byte chunk per
 //     ds_read_b128) are padded by 16 bytes, V rows (read transposed, 4 rows x
 //     64 bytes per ds_read_b64_tr_b16 half-wave) by 64 bytes;
-//   * the accumulator rescale is skipped when no row of the wave moved its max;
+//   * the accumulator rescale is skipped when no row of the wave moved its
+//     max, and in the pipelined kernel (the default) the max moves lazily and
+//     K runs one tile ahead of V so that the scores of the next tile (MFMA)
+//     overlap the softmax of the current one (VALU);
 //   * workgroups are renumbered so that all query blocks of one (batch, head)
 //     run on the same XCD (dispatch is round-robin over the 8 XCDs), letting
 //     that XCD's L2 serve the shared K/V stream; causal blocks run longest
 //     first.
+#include <type_traits>
+
 #include "fa_args.h"
 #include "fa_common.h"
 
@@ -230,9 +235,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
   }
 }
 
-// Scores of one tile for one wave: NKB 32x32 blocks S^T = K Q^T.
+// Pair-wise combine across the two half-waves (lanes l and l ^ 32) with
+// gfx950's v_permlane32_swap: a VALU exchange instead of an LDS permute.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Scores of one tile for one wave without scheduling constraints.
 template <int NKB>
-__device__ __forceinline__ void scores(f32x16* s, const half_t* Ks, const h8* qf) {
+__device__ __forceinline__ void scores_free(f32x16* s, const half_t* Ks, const h8* qf) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     h8 kf[8];
@@ -242,20 +258,82 @@ __device__ __forceinline__ void scores(f32x16* s, const half_t* Ks, const h8* qf
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], s[kb], 0, 0, 0);
-    // All eight fragment reads in flight before the first MFMA of the block.
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }
 }
 
-// Software-pipelined variant: while the softmax of tile t runs on the VALU,
-// the scores of tile t+1 are computed on the MFMA pipe, so the two overlap
-// within each wave instead of alternating.  K therefore runs one tile ahead of
-// V through LDS: iteration t loads K(t+2) and V(t+1) from HBM, computes
-// S(t+1) from K(t+1), softmax(t), then O += P(t) V(t), and stores the staged
-// tiles into the buffers that held K(t) and V(t-1).  One barrier per tile.
-template <int BN, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pp(FwdArgs a) {
+// Scores with a fixed order of LDS reads and MFMAs: the first 32-key block's
+// eight K fragments are read up front, and each score MFMA is followed by one
+// fragment read of the next block, so every read has several MFMAs' time to
+// land.  The sched_barrier fences pin that order and let only VALU, SALU and
+// global loads (the softmax of the previous tile, address arithmetic) move
+// across, into the gaps.
+template <int NKB>
+__device__ __forceinline__ void scores_ordered(f32x16* s, const half_t* Ks, const h8* qf) {
+  constexpr int kFloat = 0x2 | 0x4 | 0x20;  // VALU, SALU, VMEM read
+  h8 kf[2][8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kf[0][ks] = frag_rows_k(Ks, 0, ks * 2);
+  __builtin_amdgcn_sched_barrier(kFloat);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    s[kb] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kb & 1][ks], qf[ks], s[kb], 0, 0, 0);
+      if (kb + 1 < NKB) kf[(kb + 1) & 1][ks] = frag_rows_k(Ks, (kb + 1) * 32, ks * 2);
+      __builtin_amdgcn_sched_barrier(kFloat);
+    }
+  }
+}
+
+// O^T += V^T P^T for one tile with the same pinned order: the transposed V
+// fragments of the first 16-key step are read up front, and each MFMA is
+// followed by the reads of one fragment of the next step.
+template <int NKB>
+__device__ __forceinline__ void pv_ordered(f32x16* oacc, const half_t* Vs, const f32x16* p,
+                                           const h8* vf0) {
+  constexpr int kFloat = 0x2 | 0x4 | 0x20 | 0x200;  // VALU, SALU, VMEM read, DS write
+  constexpr int NS = NKB * 2;                       // 16-key steps per tile
+  h8 vf[2][4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) vf[0][db] = vf0[db];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const int kb = st >> 1, tt = st & 1;
+    h8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[e] = (half_t)p[kb][tt * 8 + e];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[st & 1][db], pf, oacc[db], 0, 0, 0);
+      if (st + 1 < NS)
+        vf[(st + 1) & 1][db] = frag_tr_v(Vs, ((st + 1) >> 1) * 32, (st + 1) & 1, db * 32);
+      __builtin_amdgcn_sched_barrier(kFloat);
+    }
+  }
+}
+
+// A row's running max is raised only when a tile's scores exceed it by more
+// than this many powers of two; until then probabilities are taken against
+// the stale max and stay below 2^kLazy (exact: the output's numerator and
+// denominator share that max, and 2^8 is far inside fp16 and fp32 range).
+constexpr float kLazy = 8.f;
+
+// Pipelined kernel.  K runs one tile ahead of V through LDS, so iteration t
+// holds the scores S(t+1) (MFMA) and the softmax of tile t (VALU), which do
+// not depend on each other: iteration t loads K(t+2) and V(t+1) from HBM,
+// computes S(t+1) from K(t+1), softmax(t), then O += P(t) V(t), and stores
+// the staged tiles into the buffers that held K(t) and V(t-1).  One barrier
+// per tile.  The steady-state iteration is one basic block apart from the
+// rare rescale: the global loads and LDS stores are unconditional (rows are
+// clamped in bounds; what the last iterations stage is never read), masks live
+// in a second copy of the loop that runs only the diagonal and ragged-tail
+// tiles, the running max moves lazily (kLazy) so the rescale branch is rarely
+// taken, and the half-wave max and sum use a VALU lane swap.
+// ORDERED pins the read/MFMA order (scores_ordered, pv_ordered) and reads the
+// first V fragments before the scores.
+template <int BN, int NW, bool CAUSAL, bool ORDERED>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
   constexpr int BM = 32 * NW, NT = NW * 64;
   constexpr int NKB = BN / 32;
   constexpr int TK = BN * kLSK, TV = BN * kLSV;
@@ -272,7 +350,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pp(FwdArgs a) {
   const half_t* kbase = (const half_t*)a.k.p + b * a.k.sb + h * a.k.sh;
   const half_t* vbase = (const half_t*)a.v.p + b * a.v.sb + h * a.v.sh;
 
-  const int q0 = qb * BM, qw = q0 + w * 32, qi = qw + c;
+  const int q0 = qb * BM, qi = q0 + w * 32 + c;
 
   h8 qf[8];
   {
@@ -290,6 +368,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pp(FwdArgs a) {
 
   const int kend = CAUSAL ? min(a.Sk, q0 + BM) : a.Sk;
   const int ntiles = (kend + BN - 1) / BN;
+  // Tiles [0, nfull) hold no key past the end and, causally, no key after the
+  // block's first query: no wave of the block masks them.  Every wave runs
+  // every tile of its block: a tile entirely after a wave's rows is fully
+  // masked (P = 0) and changes nothing.
+  const int nfull = min(ntiles, (CAUSAL ? min(a.Sk, q0 + 1) : a.Sk) / BN);
 
   constexpr int PER = BN * 16 / NT;
   u32x4 kr[PER], vr[PER];
@@ -297,65 +380,76 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pp(FwdArgs a) {
   tile_load<BN, NT>(vr, vbase, a.v.ss, 0, a.Sk);
   tile_store<BN, NT, kLSK>(kr, smem);
   tile_store<BN, NT, kLSV>(vr, smem + 2 * TK);
-  if (ntiles > 1) {
-    tile_load<BN, NT>(kr, kbase, a.k.ss, BN, a.Sk);
-    tile_store<BN, NT, kLSK>(kr, smem + TK);
-  }
+  tile_load<BN, NT>(kr, kbase, a.k.ss, BN, a.Sk);
+  tile_store<BN, NT, kLSK>(kr, smem + TK);
   __syncthreads();
   f32x16 scur[NKB];
-  scores<NKB>(scur, smem, qf);
+  scores_free<NKB>(scur, smem, qf);
+  // Iteration 0 overwrites K buffer 0: every wave must have read it first.
+  __syncthreads();
 
-  // Every wave runs every tile of its block: a tile entirely after a wave's
-  // rows is fully masked (P = 0) and changes nothing, and keeping the work
-  // unconditional keeps S(t+1) and softmax(t) in one basic block, where the
-  // scheduler can interleave MFMA and VALU.  In the last iteration S(t+1)
-  // reads a stale K buffer and is discarded.
-  for (int t = 0; t < ntiles; ++t) {
+  // Iteration t: stage K(t+2) and V(t+1), S(t+1) from K buffer (t+1)&1,
+  // softmax(t), O += P(t) V(t) from V buffer t&1, then store K(t+2) into K
+  // buffer t&1 (last read by S(t), one barrier ago) and V(t+1) into V buffer
+  // (t+1)&1 (last read by PV(t-1), one barrier ago).
+  auto step = [&](int t, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
     const int k0 = t * BN;
-    const bool more1 = t + 1 < ntiles, more2 = t + 2 < ntiles;
-    if (more2) tile_load<BN, NT>(kr, kbase, a.k.ss, k0 + 2 * BN, a.Sk);
-    if (more1) tile_load<BN, NT>(vr, vbase, a.v.ss, k0 + BN, a.Sk);
-    {
-      if ((k0 + BN > a.Sk) || (CAUSAL && k0 + BN - 1 > qw)) {
+    tile_load<BN, NT>(kr, kbase, a.k.ss, k0 + 2 * BN, a.Sk);
+    tile_load<BN, NT>(vr, vbase, a.v.ss, k0 + BN, a.Sk);
+    f32x16 snxt[NKB];
+    const half_t* Vs = smem + 2 * TK + (t & 1) * TV;
+    const half_t* Kn = smem + ((t + 1) & 1) * TK;
+    h8 vf0[4];
+    if constexpr (ORDERED) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + crow(r, g);
-            if (key >= a.Sk || (CAUSAL && key > qi)) scur[kb][r] = -INFINITY;
-          }
-      }
-      f32x16 snxt[NKB];
-      scores<NKB>(snxt, smem + ((t + 1) & 1) * TK, qf);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb][r]);
-      mx = fmaxf(mx, xor32(mx));
-      const float mnew = fmaxf(m, mx);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float mc = muse * cs;
-      float rs = 0.f;
+      for (int db = 0; db < 4; ++db) vf0[db] = frag_tr_v(Vs, 0, 0, db * 32);
+      scores_ordered<NKB>(snxt, Kn, qf);
+    } else {
+      scores_free<NKB>(snxt, Kn, qf);
+    }
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(scur[kb][r], cs, -mc));
-          scur[kb][r] = p;
-          rs += p;
+          const int key = k0 + kb * 32 + crow(r, g);
+          if (key >= a.Sk || (CAUSAL && key > qi)) scur[kb][r] = -INFINITY;
         }
-      if (__any(mnew != m)) {
-        const float alpha = fast_exp2((m - muse) * cs);
-        lsum *= alpha;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[kb][r]);
+    mx = max_xor32(mx);
+    // m = -inf and a finite mx give +inf > kLazy: the first scores always
+    // raise the max.  Both -inf (a row with no key yet) give NaN: no raise.
+    const bool raise = (mx - m) * cs > kLazy;
+    const float mnew = raise ? mx : m;
+    const float mc = (mnew == -INFINITY ? 0.f : mnew) * cs;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(scur[kb][r], cs, -mc));
+        scur[kb][r] = p;
+        rs += p;
       }
-      lsum += rs;
-      m = mnew;
-      const half_t* Vs = smem + 2 * TK + (t & 1) * TV;
+    if (__any(raise)) {
+      const float alpha = raise ? fast_exp2((m - mnew) * cs) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    lsum += rs;
+    m = mnew;
+    if constexpr (ORDERED) {
+      pv_ordered<NKB>(oacc, Vs, scur, vf0);
+    } else {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -370,15 +464,18 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pp(FwdArgs a) {
           for (int db = 0; db < 4; ++db)
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pf, oacc[db], 0, 0, 0);
         }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) scur[kb] = snxt[kb];
     }
-    if (more2) tile_store<BN, NT, kLSK>(kr, smem + (t & 1) * TK);
-    if (more1) tile_store<BN, NT, kLSV>(vr, smem + 2 * TK + ((t + 1) & 1) * TV);
+    tile_store<BN, NT, kLSK>(kr, smem + (t & 1) * TK);
+    tile_store<BN, NT, kLSV>(vr, smem + 2 * TK + ((t + 1) & 1) * TV);
     __syncthreads();
-  }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) scur[kb] = snxt[kb];
+  };
+  int t = 0;
+  for (; t < nfull; ++t) step(t, std::false_type{});
+  for (; t < ntiles; ++t) step(t, std::true_type{});
 
-  const float ltot = lsum + xor32(lsum);
+  const float ltot = add_xor32(lsum);
   if (qi < a.Sq) {
     const float inv = 1.f / ltot;
     half_t* orow = (half_t*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
@@ -396,46 +493,44 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pp(FwdArgs a) {
   }
 }
 
-template <int BN, int NW, bool CAUSAL>
-hipError_t launch_pp(const FwdArgs& a, hipStream_t s) {
-  constexpr int BM = 32 * NW;
+template <class Kernel>
+hipError_t launch_k(Kernel* k, int BM, int threads, const FwdArgs& a, hipStream_t s) {
   const int64_t grid = (((int64_t)a.Sq + BM - 1) / BM) * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_f16_d128_pp<BN, NW, CAUSAL>),
-                         dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid), dim3(threads),
+                         args, 0, s);
 }
 
-template <int BN, int NW, bool CAUSAL>
-hipError_t launch(const FwdArgs& a, hipStream_t s) {
-  constexpr int BM = 32 * NW;
-  const int64_t grid = (((int64_t)a.Sq + BM - 1) / BM) * a.B * a.H;
-  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_f16_d128<BN, NW, CAUSAL>),
-                         dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
+template <int BN, int NW, bool ORDERED>
+hipError_t launch_pipe(const FwdArgs& a, int causal, hipStream_t s) {
+  return causal ? launch_k(&fwd_f16_d128_pipe<BN, NW, true, ORDERED>, 32 * NW, NW * 64, a, s)
+                : launch_k(&fwd_f16_d128_pipe<BN, NW, false, ORDERED>, 32 * NW, NW * 64, a, s);
+}
+
+template <int BN, int NW>
+hipError_t launch_plain(const FwdArgs& a, int causal, hipStream_t s) {
+  return causal ? launch_k(&fwd_f16_d128<BN, NW, true>, 32 * NW, NW * 64, a, s)
+                : launch_k(&fwd_f16_d128<BN, NW, false>, 32 * NW, NW * 64, a, s);
 }
 
 }  // namespace
 
-// Variants: 0 = (BN 64, 4 waves), 1 = (BN 64, 8 waves), 2 = (BN 128, 4 waves);
-// software-pipelined: 3 = (BN 64, 8 waves), 4 = (BN 32, 8 waves), 5 = (BN 64, 4 waves).
-int fwd_fast_variants() { return 6; }
+// Variants (BN keys per tile, waves): pipelined 0 = (64, 8, ordered),
+// 1 = (64, 8); plain 2 = (64, 8), 3 = (64, 4).
+int fwd_fast_variants() { return 4; }
 
 TileCfg fwd_fast_cfg(int v) {
-  const int bn = v == 2 ? 128 : v == 4 ? 32 : 64;
-  const int nw = (v == 1 || v == 3 || v == 4) ? 8 : 4;
-  return TileCfg{32 * nw, bn, nw, 2 * bn * (kLSK + kLSV) * 2};
+  const int nw = v == 3 ? 4 : 8;
+  return TileCfg{32 * nw, 64, nw, 2 * 64 * (kLSK + kLSV) * 2};
 }
 
 hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int causal, hipStream_t s) {
   switch (variant) {
-    case 0: return causal ? launch<64, 4, true>(a, s) : launch<64, 4, false>(a, s);
-    case 1: return causal ? launch<64, 8, true>(a, s) : launch<64, 8, false>(a, s);
-    case 2: return causal ? launch<128, 4, true>(a, s) : launch<128, 4, false>(a, s);
-    case 3: return causal ? launch_pp<64, 8, true>(a, s) : launch_pp<64, 8, false>(a, s);
-    case 4: return causal ? launch_pp<32, 8, true>(a, s) : launch_pp<32, 8, false>(a, s);
-    case 5: return causal ? launch_pp<64, 4, true>(a, s) : launch_pp<64, 4, false>(a, s);
+    case 0: return launch_pipe<64, 8, true>(a, causal, s);
+    case 1: return launch_pipe<64, 8, false>(a, causal, s);
+    case 2: return launch_plain<64, 8>(a, causal, s);
+    case 3: return launch_plain<64, 4>(a, causal, s);
   }
   return hipErrorInvalidValue;
 }

@@ -22,10 +22,11 @@ def _fa():
     return fa
 
 
-def run_case(case, tiles=(-1, -1, -1), layout_out=None):
-    """Run fa_fwd + fa_bwd for a workload case; returns host float64 results."""
+def run_case(case, tiles=(-1, -1, -1), layout_out=None, x=None):
+    """Run fa_fwd + fa_bwd for a workload case (inputs from the case's seeded
+    generator unless ``x`` is given); returns the inputs and host results."""
     fa = _fa()
-    x = W.make_inputs(case)
+    x = W.make_inputs(case) if x is None else x
     dq_t = {n: U.to_device(a) for n, a in x.items()}
     tdt = U.torch_dtype(case.dtype)
     lay = layout_out or case.layout
@@ -103,6 +104,35 @@ EXTRA = [
 @pytest.mark.parametrize("case", EXTRA, ids=lambda c: c.name)
 def test_extra_shapes(case):
     x, got = run_case(case)
+    check_full(case, x, got)
+
+
+def _rising_inputs(case, growth):
+    """Keys scaled up along the sequence, so that every query row's running
+    maximum rises many times while the keys stream past (the online-softmax
+    rescale path, taken whenever a tile raises a row maximum)."""
+    x = W.make_inputs(case)
+    ramp = (1.0 + growth * np.arange(case.Sk) / max(1, case.Sk - 1)).astype(np.float64)
+    k = x["k"].astype(np.float64) * ramp[None, None, :, None]
+    x["k"] = k.astype(x["k"].dtype)
+    return x
+
+
+RISING = [(dname, D, causal, t) for dname, D in (("f16", 128), ("f16", 64), ("f32", 64))
+          for causal in (False, True) for t in range(4 if (dname, D) == ("f16", 128) else 1)]
+
+
+@pytest.mark.parametrize("dname,D,causal,t", RISING,
+                         ids=[f"{d}-D{D}-{'c' if c else 'nc'}-t{t}" for d, D, c, t in RISING])
+def test_rising_scores_rescale(dname, D, causal, t):
+    """Scores grow along the keys (running maxima rise by far more than the
+    forward's lazy-rescale threshold over the sequence); every fp16 D=128
+    forward variant is forced in turn."""
+    case = W.Case(f"rising_{dname}_D{D}_{causal}", 1, 2, 700, 700, D, dname, causal,
+                  seed=300 + D, q_mult=4.0)
+    fa = _fa()
+    nf = fa.fa_tile_count(fa.FA_PASS_FWD, 0 if dname == "f16" else 1, D)
+    x, got = run_case(case, tiles=(t % nf, -1, -1), x=_rising_inputs(case, 3.0))
     check_full(case, x, got)
 
 
