@@ -39,6 +39,8 @@ def parse():
                     help="only run a plain 512 MiB device-to-device copy (for scaling HBM counters)")
     ap.add_argument("--sweep", default="",
                     help="optional path: also time the fp16 length sweep and write JSON lines there")
+    ap.add_argument("--no-bf16", action="store_true",
+                    help="skip the secondary bfloat16 timing of the same workload")
     return ap.parse_args()
 
 
@@ -51,6 +53,8 @@ def make_device_inputs(case, torch):
     from exact_attention_88_amd import workloads as W
     x = W.make_inputs(case)
     dev = {n: torch.from_numpy(a.copy()).to("cuda") for n, a in x.items()}
+    if case.dtype == "bf16":  # float32 arrays holding bfloat16 values: exact cast
+        dev = {n: t.to(torch.bfloat16) for n, t in dev.items()}
     return x, dev
 
 
@@ -209,6 +213,19 @@ def main():
                      "frac": round(achieved / MFMA_PEAK_F16, 4),
                      "traffic": measured_traffic(dom)},
     }
+    if not args.no_bf16:
+        # Secondary figure: the same workload in bfloat16 (inputs rounded to
+        # bfloat16 from the same draws), same accounting.
+        import dataclasses
+        bcase = dataclasses.replace(case, name="long_bf16_causal", dtype="bf16")
+        _, bdev = make_device_inputs(bcase, torch)
+        bsteps = max(3, args.steps // 2)
+        bwall, bavg = time_path(fa, torch, bcase, bdev, bsteps, args.warmup)
+        line["bf16"] = {"fwd_tflops": round(ff / (bavg["fwd"] * 1e-3) / 1e12, 2),
+                        "fwdbwd_tflops": round(3.5 * ff / (bwall / bsteps) / 1e12, 2),
+                        "ms_per_step": round(bwall / bsteps * 1e3, 4), "steps": bsteps,
+                        "kernel_ms": {n: round(v, 4) for n, v in bavg.items()}}
+        del bdev
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, x, args.cpu_heads)
     if args.sweep:

@@ -25,9 +25,9 @@ int hip_status(hipError_t e) {
   return FA_ERR_HIP;
 }
 
-bool valid_dtype(int dt) { return dt == FA_F16 || dt == FA_F32; }
+bool valid_dtype(int dt) { return dt == FA_F16 || dt == FA_F32 || dt == FA_BF16; }
 bool valid_d(int64_t D) { return D == 16 || D == 32 || D == 64 || D == 128; }
-int esize(int dt) { return dt == FA_F16 ? 2 : 4; }
+int esize(int dt) { return dt == FA_F32 ? 4 : 2; }
 
 bool strides_ok(const int64_t* s) {
   return s != nullptr && s[0] >= 0 && s[1] >= 0 && s[2] >= 0 && s[3] >= 0;

@@ -43,17 +43,22 @@ struct TileCfg {
   int lds;    // static LDS bytes
 };
 
-// Per-pass tile tables (index = tile id) for a dtype (0 = f16, 1 = f32) and
-// head dim; count returns the number of entries.
+// Element dtypes (the fa_dtype values): 0 = f16, 1 = f32, 2 = bf16.  The two
+// 16-bit types share tile tables and kernel shapes.
+constexpr int table_dt(int dtype) { return dtype == 1 ? 1 : 0; }
+constexpr int elem_size(int dtype) { return dtype == 1 ? 4 : 2; }
+
+// Per-pass tile tables (index = tile id) for a dtype and head dim; count
+// returns the number of entries.
 int fwd_tile_count(int dtype, int D);
 const TileCfg* fwd_tile(int dtype, int D, int id);
 int fwd_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s);
 
-// Tuned fp16 / head-dim-128 forward (fa_fwd_f16.hip).
+// Tuned 16-bit (fp16 and bf16) head-dim-128 forward (fa_fwd_f16.hip).
 int fwd_fast_variants();
 TileCfg fwd_fast_cfg(int variant);
-hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int causal, hipStream_t s);
+hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int dtype, int causal, hipStream_t s);
 
 int dkdv_tile_count(int dtype, int D);
 const TileCfg* dkdv_tile(int dtype, int D, int id);
@@ -70,9 +75,9 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int D, hipStream_t s);
 // Tuned fp16 / head-dim-128 backward kernels (fa_bwd_f16.hip).
 int dq_fast_variants();
 TileCfg dq_fast_cfg(int variant);
-hipError_t launch_dq_fast(const BwdArgs& a, int variant, int causal, hipStream_t s);
+hipError_t launch_dq_fast(const BwdArgs& a, int variant, int dtype, int causal, hipStream_t s);
 int dkdv_fast_variants();
 TileCfg dkdv_fast_cfg(int variant);
-hipError_t launch_dkdv_fast(const BwdArgs& a, int variant, int causal, hipStream_t s);
+hipError_t launch_dkdv_fast(const BwdArgs& a, int variant, int dtype, int causal, hipStream_t s);
 
 }  // namespace fa

@@ -241,10 +241,10 @@ hipError_t dispatch(const BwdArgs& a, int raw, int causal, hipStream_t s) {
 
 int raw_for(int dtype, int D, int id) {
   switch (D) {
-    case 16: return raw_index(dtype, 16, id);
-    case 32: return raw_index(dtype, 32, id);
-    case 64: return raw_index(dtype, 64, id);
-    case 128: return raw_index(dtype, 128, id);
+    case 16: return raw_index(table_dt(dtype), 16, id);
+    case 32: return raw_index(table_dt(dtype), 32, id);
+    case 64: return raw_index(table_dt(dtype), 64, id);
+    case 128: return raw_index(table_dt(dtype), 128, id);
   }
   return -1;
 }
@@ -264,7 +264,7 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
 
 // fp16 with head dim 128 puts the tuned kernel's variants (fa_bwd_f16.hip)
 // first in its table; the generic entries follow.
-static int fast_count(int dtype, int D) { return (dtype == 0 && D == 128) ? dkdv_fast_variants() : 0; }
+static int fast_count(int dtype, int D) { return (table_dt(dtype) == 0 && D == 128) ? dkdv_fast_variants() : 0; }
 
 static int generic_count(int dtype, int D) {
   switch (D) {
@@ -287,8 +287,8 @@ const TileCfg* dkdv_tile(int dtype, int D, int id) {
     return &cfg;
   }
   id -= nf;
-  const Tile t = tile_at(dtype, raw_for(dtype, D, id));
-  cfg = TileCfg{t.bm, 32 * t.nw, t.nw, lds_bytes(dtype == 0 ? 2 : 4, D, t.bm)};
+  const Tile t = tile_at(table_dt(dtype), raw_for(dtype, D, id));
+  cfg = TileCfg{t.bm, 32 * t.nw, t.nw, lds_bytes(elem_size(dtype), D, t.bm)};
   return &cfg;
 }
 
@@ -297,7 +297,7 @@ int dkdv_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
   // fp16, D = 128: the tuned kernel with 128-query tiles in the swizzled
   // single-copy layout measured fastest on MI355X at S = 4096 and 16384,
   // causal and not.
-  if (dtype == 0 && D == 128) return 3;
+  if (table_dt(dtype) == 0 && D == 128) return 3;
   return 0;
 }
 
@@ -307,7 +307,7 @@ hipError_t launch_dkdv(const BwdArgs& a, int dtype, int D, int causal, int tile,
     // The tuned kernel needs 16-byte vector access to every tensor it touches;
     // other layouts run the generic kernel's first entry instead.
     const int need = VEC_Q | VEC_K | VEC_V | VEC_DO | VEC_DK | VEC_DV;
-    if ((a.vec & need) == need) return launch_dkdv_fast(a, tile, causal, s);
+    if ((a.vec & need) == need) return launch_dkdv_fast(a, tile, dtype, causal, s);
     tile = nf;
   }
   const int raw = raw_for(dtype, D, tile - nf);
@@ -318,6 +318,13 @@ hipError_t launch_dkdv(const BwdArgs& a, int dtype, int D, int causal, int tile,
       case 32: return dispatch<half_t, 32>(a, raw, causal, s);
       case 64: return dispatch<half_t, 64>(a, raw, causal, s);
       case 128: return dispatch<half_t, 128>(a, raw, causal, s);
+    }
+  } else if (dtype == 2) {
+    switch (D) {
+      case 16: return dispatch<bf16_t, 16>(a, raw, causal, s);
+      case 32: return dispatch<bf16_t, 32>(a, raw, causal, s);
+      case 64: return dispatch<bf16_t, 64>(a, raw, causal, s);
+      case 128: return dispatch<bf16_t, 128>(a, raw, causal, s);
     }
   } else {
     switch (D) {
@@ -337,6 +344,13 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int D, hipStream_t s) {
       case 32: return launch_pre_t<half_t, 32>(a, s);
       case 64: return launch_pre_t<half_t, 64>(a, s);
       case 128: return launch_pre_t<half_t, 128>(a, s);
+    }
+  } else if (dtype == 2) {
+    switch (D) {
+      case 16: return launch_pre_t<bf16_t, 16>(a, s);
+      case 32: return launch_pre_t<bf16_t, 32>(a, s);
+      case 64: return launch_pre_t<bf16_t, 64>(a, s);
+      case 128: return launch_pre_t<bf16_t, 128>(a, s);
     }
   } else {
     switch (D) {

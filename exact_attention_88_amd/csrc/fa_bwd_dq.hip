@@ -179,10 +179,10 @@ hipError_t dispatch(const BwdArgs& a, int raw, int causal, hipStream_t s) {
 
 int raw_for(int dtype, int D, int id) {
   switch (D) {
-    case 16: return raw_index(dtype, 16, id);
-    case 32: return raw_index(dtype, 32, id);
-    case 64: return raw_index(dtype, 64, id);
-    case 128: return raw_index(dtype, 128, id);
+    case 16: return raw_index(table_dt(dtype), 16, id);
+    case 32: return raw_index(table_dt(dtype), 32, id);
+    case 64: return raw_index(table_dt(dtype), 64, id);
+    case 128: return raw_index(table_dt(dtype), 128, id);
   }
   return -1;
 }
@@ -191,7 +191,7 @@ int raw_for(int dtype, int D, int id) {
 
 // fp16 with head dim 128 puts the tuned kernel's variants (fa_bwd_f16.hip)
 // first in its table; the generic entries follow.
-static int fast_count(int dtype, int D) { return (dtype == 0 && D == 128) ? dq_fast_variants() : 0; }
+static int fast_count(int dtype, int D) { return (table_dt(dtype) == 0 && D == 128) ? dq_fast_variants() : 0; }
 
 static int generic_count(int dtype, int D) {
   switch (D) {
@@ -214,8 +214,8 @@ const TileCfg* dq_tile(int dtype, int D, int id) {
     return &cfg;
   }
   id -= nf;
-  const Tile t = tile_at(dtype, raw_for(dtype, D, id));
-  cfg = TileCfg{32 * t.nw, t.bn, t.nw, lds_bytes(dtype == 0 ? 2 : 4, D, t.bn)};
+  const Tile t = tile_at(table_dt(dtype), raw_for(dtype, D, id));
+  cfg = TileCfg{32 * t.nw, t.bn, t.nw, lds_bytes(elem_size(dtype), D, t.bn)};
   return &cfg;
 }
 
@@ -224,7 +224,7 @@ int dq_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
   // fp16, D = 128: the tuned kernel with 8 waves and 64-key tiles in the
   // swizzled single-copy layout measured fastest on MI355X at S = 4096 and
   // 16384, causal and not.
-  if (dtype == 0 && D == 128) return 4;
+  if (table_dt(dtype) == 0 && D == 128) return 4;
   return 0;
 }
 
@@ -234,7 +234,7 @@ hipError_t launch_dq(const BwdArgs& a, int dtype, int D, int causal, int tile, h
     // The tuned kernel needs 16-byte vector access to every tensor it touches;
     // other layouts run the generic kernel's first entry instead.
     const int need = VEC_Q | VEC_K | VEC_V | VEC_DO | VEC_DQ;
-    if ((a.vec & need) == need) return launch_dq_fast(a, tile, causal, s);
+    if ((a.vec & need) == need) return launch_dq_fast(a, tile, dtype, causal, s);
     tile = nf;
   }
   const int raw = raw_for(dtype, D, tile - nf);
@@ -245,6 +245,13 @@ hipError_t launch_dq(const BwdArgs& a, int dtype, int D, int causal, int tile, h
       case 32: return dispatch<half_t, 32>(a, raw, causal, s);
       case 64: return dispatch<half_t, 64>(a, raw, causal, s);
       case 128: return dispatch<half_t, 128>(a, raw, causal, s);
+    }
+  } else if (dtype == 2) {
+    switch (D) {
+      case 16: return dispatch<bf16_t, 16>(a, raw, causal, s);
+      case 32: return dispatch<bf16_t, 32>(a, raw, causal, s);
+      case 64: return dispatch<bf16_t, 64>(a, raw, causal, s);
+      case 128: return dispatch<bf16_t, 128>(a, raw, causal, s);
     }
   } else {
     switch (D) {

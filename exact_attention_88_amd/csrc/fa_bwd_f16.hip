@@ -1,5 +1,5 @@
-// Backward dK/dV and dQ kernels for fp16 with head dim 128 on gfx950: the
-// tuned path.
+// Backward dK/dV and dQ kernels for 16-bit inputs (fp16, bf16) with head dim
+// 128 on gfx950: the tuned path.
 //
 // Same method as the generic backward kernels ("Triton FlashAttention": the
 // FlashAttention-2 split into a dK/dV kernel and a dQ kernel with no atomics,
@@ -38,8 +38,8 @@ __device__ __forceinline__ int xcd_logical_block() {
   return (id % 8) * (n / 8) + id / 8;
 }
 
-template <int ROWS, int NT>
-__device__ __forceinline__ void tile_load(u32x4* r, const half_t* __restrict__ base, int64_t ss,
+template <int ROWS, int NT, class T>
+__device__ __forceinline__ void tile_load(u32x4* r, const T* __restrict__ base, int64_t ss,
                                           int row0, int nrows) {
   constexpr int PER = ROWS * 16 / NT;
 #pragma unroll
@@ -50,8 +50,8 @@ __device__ __forceinline__ void tile_load(u32x4* r, const half_t* __restrict__ b
   }
 }
 
-template <int ROWS, int NT, int LS>
-__device__ __forceinline__ void tile_store(const u32x4* r, half_t* lds) {
+template <int ROWS, int NT, int LS, class T>
+__device__ __forceinline__ void tile_store(const u32x4* r, T* lds) {
   constexpr int PER = ROWS * 16 / NT;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -61,23 +61,25 @@ __device__ __forceinline__ void tile_store(const u32x4* r, half_t* lds) {
 }
 
 // Row-wise fragment (row-read layout): lane (c, g) gets row rbase + c, chunk kchunk + g.
-__device__ __forceinline__ h8 frag_r(const half_t* lds, int rbase, int kchunk) {
+template <class T>
+__device__ __forceinline__ V8<T> frag_r(const T* lds, int rbase, int kchunk) {
   const int lane = threadIdx.x & 63;
-  return *reinterpret_cast<const h8*>(lds + (rbase + (lane & 31)) * kLSR +
+  return *reinterpret_cast<const V8<T>*>(lds + (rbase + (lane & 31)) * kLSR +
                                       (kchunk + (lane >> 5)) * 8);
 }
 
 // Transposed fragment (transposed-read layout); see frag_tr in fa_common.h.
-__device__ __forceinline__ h8 frag_t(const half_t* lds, int rbase, int t, int cbase) {
+template <class T>
+__device__ __forceinline__ V8<T> frag_t(const T* lds, int rbase, int t, int cbase) {
   const int lane = threadIdx.x & 63, g = lane >> 5, j = lane & 15;
   const int col = cbase + ((lane >> 4) & 1) * 16 + (j & 3) * 4;
   const int row = rbase + t * 16 + g * 4 + (j >> 2);
   typedef __attribute__((address_space(3))) s4 lds_s4;
-  const half_t* p0 = lds + row * kLST + col;
+  const T* p0 = lds + row * kLST + col;
   s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
   s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + 8 * kLST));
-  h4 ah = __builtin_bit_cast(h4, a), bh = __builtin_bit_cast(h4, b);
-  h8 r;
+  V4<T> ah = __builtin_bit_cast(V4<T>, a), bh = __builtin_bit_cast(V4<T>, b);
+  V8<T> r;
   r[0] = ah[0]; r[1] = ah[1]; r[2] = ah[2]; r[3] = ah[3];
   r[4] = bh[0]; r[5] = bh[1]; r[6] = bh[2]; r[7] = bh[3];
   return r;
@@ -91,8 +93,8 @@ __device__ __forceinline__ h8 frag_t(const half_t* lds, int rbase, int t, int cb
 // transposed reads are conflict free).  One layout serves both read patterns.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-template <int ROWS, int NT>
-__device__ __forceinline__ void tile_store_swz(const u32x4* r, half_t* lds) {
+template <int ROWS, int NT, class T>
+__device__ __forceinline__ void tile_store_swz(const u32x4* r, T* lds) {
   constexpr int PER = ROWS * 16 / NT;
   static_assert(NT % 256 == 0, "every thread keeps its row residue mod 16");
   const int row0 = (int)threadIdx.x >> 4, off = row0 * kD + (((threadIdx.x & 15) ^ swz(row0)) << 3);
@@ -101,63 +103,64 @@ __device__ __forceinline__ void tile_store_swz(const u32x4* r, half_t* lds) {
 }
 
 // Row-wise fragment in the swizzled layout; rbase is a multiple of 16.
-__device__ __forceinline__ h8 frag_r_swz(const half_t* lds, int rbase, int kchunk) {
+template <class T>
+__device__ __forceinline__ V8<T> frag_r_swz(const T* lds, int rbase, int kchunk) {
   const int lane = threadIdx.x & 63, r = lane & 31;
-  return *reinterpret_cast<const h8*>(lds + (rbase + r) * kD +
+  return *reinterpret_cast<const V8<T>*>(lds + (rbase + r) * kD +
                                       (((kchunk + (lane >> 5)) ^ swz(r)) << 3));
 }
 
 // Transposed fragment in the swizzled layout (same lanes as frag_t); rbase is
 // a multiple of 16 and cbase of 8.
-__device__ __forceinline__ h8 frag_t_swz(const half_t* lds, int rbase, int t, int cbase) {
+template <class T>
+__device__ __forceinline__ V8<T> frag_t_swz(const T* lds, int rbase, int t, int cbase) {
   const int lane = threadIdx.x & 63, g = lane >> 5, j = lane & 15;
   const int col = ((lane >> 4) & 1) * 16 + (j & 3) * 4;
   const int r = g * 4 + (j >> 2);
   const int ch = (cbase >> 3) + (col >> 3);
   typedef __attribute__((address_space(3))) s4 lds_s4;
-  const half_t* p0 = lds + (rbase + t * 16 + r) * kD + ((ch ^ swz(r)) << 3) + (col & 7);
-  const half_t* p1 = lds + (rbase + t * 16 + r + 8) * kD + ((ch ^ swz(r + 8)) << 3) + (col & 7);
+  const T* p0 = lds + (rbase + t * 16 + r) * kD + ((ch ^ swz(r)) << 3) + (col & 7);
+  const T* p1 = lds + (rbase + t * 16 + r + 8) * kD + ((ch ^ swz(r + 8)) << 3) + (col & 7);
   s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
   s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1));
-  h4 ah = __builtin_bit_cast(h4, a), bh = __builtin_bit_cast(h4, b);
-  h8 x;
+  V4<T> ah = __builtin_bit_cast(V4<T>, a), bh = __builtin_bit_cast(V4<T>, b);
+  V8<T> x;
   x[0] = ah[0]; x[1] = ah[1]; x[2] = ah[2]; x[3] = ah[3];
   x[4] = bh[0]; x[5] = bh[1]; x[6] = bh[2]; x[7] = bh[3];
   return x;
 }
 
-__device__ __forceinline__ f32x16 mma(h8 a, h8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ h8 cvt8(const f32x16& x, int t) {
-  h8 r;
+// Accumulator registers t*8 .. t*8+7 rounded to T (round to nearest even).
+template <class T>
+__device__ __forceinline__ V8<T> cvt8(const f32x16& x, int t) {
+  V8<T> r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (half_t)x[t * 8 + e];
+  for (int e = 0; e < 8; ++e) r[e] = (T)x[t * 8 + e];
   return r;
 }
 
-__device__ __forceinline__ void store_row4x4(half_t* rowp, const f32x16* acc, float mul, int g) {
+template <class T>
+__device__ __forceinline__ void store_row4x4(T* rowp, const f32x16* acc, float mul, int g) {
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      h4 v;
+      V4<T> v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (half_t)(acc[db][r4 * 4 + e] * mul);
-      *reinterpret_cast<h4*>(rowp + db * 32 + r4 * 8 + g * 4) = v;
+      for (int e = 0; e < 4; ++e) v[e] = (T)(acc[db][r4 * 4 + e] * mul);
+      *reinterpret_cast<V4<T>*>(rowp + db * 32 + r4 * 8 + g * 4) = v;
     }
 }
 
 // ------------------------------------------------------------------- dQ
 // SWZ: K and V are stored once each in the swizzled layout (K serves both its
 // row-wise and its transposed reads) instead of K twice in the padded layouts.
-template <int BN, int NW, bool CAUSAL, bool SWZ>
+template <class T, int BN, int NW, bool CAUSAL, bool SWZ>
 __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
   constexpr int BM = 32 * NW, NT = NW * 64, NKB = BN / 32;
   constexpr int TR = SWZ ? BN * kD : BN * kLSR, TT = SWZ ? 0 : BN * kLST;
   constexpr int BUF = 2 * TR + TT;  // K rows, V rows[, K transposed]
-  __shared__ __attribute__((aligned(1024))) half_t smem[2 * BUF];
+  __shared__ __attribute__((aligned(1024))) T smem[2 * BUF];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nqb = (a.Sq + BM - 1) / BM;
@@ -166,21 +169,21 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
   const int bh = L / nqb;
   if (CAUSAL) qb = nqb - 1 - qb;
   const int b = bh / a.H, h = bh % a.H;
-  const half_t* kbase = (const half_t*)a.k.p + b * a.k.sb + h * a.k.sh;
-  const half_t* vbase = (const half_t*)a.v.p + b * a.v.sb + h * a.v.sh;
+  const T* kbase = (const T*)a.k.p + b * a.k.sb + h * a.k.sh;
+  const T* vbase = (const T*)a.v.p + b * a.v.sb + h * a.v.sh;
   const int q0 = qb * BM, qw = q0 + w * 32, qi = qw + c;
   const bool valid = qi < a.Sq;
 
-  h8 qf[8], df[8];
+  V8<T> qf[8], df[8];
   {
     const int qc = min(qi, a.Sq - 1);
-    const half_t* qrow = (const half_t*)a.q.p + b * a.q.sb + h * a.q.sh + (int64_t)qc * a.q.ss;
-    const half_t* drow =
-        (const half_t*)a.dout.p + b * a.dout.sb + h * a.dout.sh + (int64_t)qc * a.dout.ss;
+    const T* qrow = (const T*)a.q.p + b * a.q.sb + h * a.q.sh + (int64_t)qc * a.q.ss;
+    const T* drow =
+        (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh + (int64_t)qc * a.dout.ss;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      qf[ks] = *reinterpret_cast<const h8*>(qrow + ks * 16 + g * 8);
-      df[ks] = *reinterpret_cast<const h8*>(drow + ks * 16 + g * 8);
+      qf[ks] = *reinterpret_cast<const V8<T>*>(qrow + ks * 16 + g * 8);
+      df[ks] = *reinterpret_cast<const V8<T>*>(drow + ks * 16 + g * 8);
     }
   }
   const float lse2 = valid ? a.lse[(int64_t)bh * a.Sq + qi] * kLog2e : INFINITY;
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
   u32x4 kr[PER], vr[PER];
   tile_load<BN, NT>(kr, kbase, a.k.ss, 0, a.Sk);
   tile_load<BN, NT>(vr, vbase, a.v.ss, 0, a.Sk);
-  auto store_tiles = [&](half_t* nb) {
+  auto store_tiles = [&](T* nb) {
     if constexpr (SWZ) {
       tile_store_swz<BN, NT>(kr, nb);
       tile_store_swz<BN, NT>(vr, nb + TR);
@@ -212,9 +215,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
 
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BN;
-    const half_t* Kr = smem + (t & 1) * BUF;
-    const half_t* Vr = Kr + TR;
-    const half_t* Kt = SWZ ? Kr : Kr + 2 * TR;
+    const T* Kr = smem + (t & 1) * BUF;
+    const T* Vr = Kr + TR;
+    const T* Kt = SWZ ? Kr : Kr + 2 * TR;
     __syncthreads();
     const bool more = t + 1 < ntiles;
     if (more) {
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
       if (CAUSAL && ks0 > qw + 31) continue;
       // Row-wise operands of S^T and dP^T first, then the transposed K operand
       // of dQ (one k-step at a time: with 8 waves a wave has 256 registers).
-      h8 kf[8], vf[8];
+      V8<T> kf[8], vf[8];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         kf[ks] = SWZ ? frag_r_swz(Kr, kb * 32, ks * 2) : frag_r(Kr, kb * 32, ks * 2);
@@ -236,9 +239,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
         vf[ks] = SWZ ? frag_r_swz(Vr, kb * 32, ks * 2) : frag_r(Vr, kb * 32, ks * 2);
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s = mma(kf[ks], qf[ks], s);
+      for (int ks = 0; ks < 8; ++ks) s = Mfma<T>::mma(kf[ks], qf[ks], s);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) dp = mma(vf[ks], df[ks], dp);
+      for (int ks = 0; ks < 8; ++ks) dp = Mfma<T>::mma(vf[ks], df[ks], dp);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = fast_exp2(__builtin_fmaf(s[r], cs, -lse2));
       // Masks only on the diagonal block and the ragged key tail.
@@ -253,20 +256,20 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
       for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - dlt);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        h8 kt[4];
+        V8<T> kt[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db)
           kt[db] = SWZ ? frag_t_swz(Kt, kb * 32, tt, db * 32) : frag_t(Kt, kb * 32, tt, db * 32);
-        const h8 sf = cvt8(s, tt);
+        const V8<T> sf = cvt8<T>(s, tt);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dq[db] = mma(kt[db], sf, dq[db]);
+        for (int db = 0; db < 4; ++db) dq[db] = Mfma<T>::mma(kt[db], sf, dq[db]);
       }
     }
     if (more) store_tiles(smem + ((t + 1) & 1) * BUF);
   }
 
   if (valid) {
-    half_t* row = (half_t*)a.dq.p + b * a.dq.sb + h * a.dq.sh + (int64_t)qi * a.dq.ss;
+    T* row = (T*)a.dq.p + b * a.dq.sb + h * a.dq.sh + (int64_t)qi * a.dq.ss;
     store_row4x4(row, dq, a.scale, g);
   }
 }
@@ -274,12 +277,12 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
 // ------------------------------------------------------------------- dK / dV
 // SWZ: Q and dO are stored once each in the swizzled layout instead of twice
 // in the padded layouts.
-template <int BM, int NW, bool CAUSAL, bool SWZ>
+template <class T, int BM, int NW, bool CAUSAL, bool SWZ>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   constexpr int BN = 32 * NW, NT = NW * 64, NQB = BM / 32;
   constexpr int TR = SWZ ? BM * kD : BM * kLSR, TT = SWZ ? 0 : BM * kLST;
   constexpr int BUF = 2 * TR + 2 * TT;  // Q rows, dO rows[, Q transposed, dO transposed]
-  __shared__ __attribute__((aligned(1024))) half_t smem[2 * BUF];
+  __shared__ __attribute__((aligned(1024))) T smem[2 * BUF];
   __shared__ __attribute__((aligned(16))) float lsd[2][2][BM];  // [buffer][LSE*log2e, delta][row]
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
@@ -288,21 +291,21 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   const int kb = L % nkb;  // causal: lowest key blocks (most work) first
   const int bh = L / nkb;
   const int b = bh / a.H, h = bh % a.H;
-  const half_t* qbase = (const half_t*)a.q.p + b * a.q.sb + h * a.q.sh;
-  const half_t* dobase = (const half_t*)a.dout.p + b * a.dout.sb + h * a.dout.sh;
+  const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
+  const T* dobase = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh;
   const float* lse = a.lse + (int64_t)bh * a.Sq;
   const float* dl = a.delta + (int64_t)bh * a.Sq;
   const int k0 = kb * BN, kw = k0 + w * 32, kj = kw + c;
 
-  h8 kf[8], vf[8];
+  V8<T> kf[8], vf[8];
   {
     const int kc = min(kj, a.Sk - 1);
-    const half_t* krow = (const half_t*)a.k.p + b * a.k.sb + h * a.k.sh + (int64_t)kc * a.k.ss;
-    const half_t* vrow = (const half_t*)a.v.p + b * a.v.sb + h * a.v.sh + (int64_t)kc * a.v.ss;
+    const T* krow = (const T*)a.k.p + b * a.k.sb + h * a.k.sh + (int64_t)kc * a.k.ss;
+    const T* vrow = (const T*)a.v.p + b * a.v.sb + h * a.v.sh + (int64_t)kc * a.v.ss;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      kf[ks] = *reinterpret_cast<const h8*>(krow + ks * 16 + g * 8);
-      vf[ks] = *reinterpret_cast<const h8*>(vrow + ks * 16 + g * 8);
+      kf[ks] = *reinterpret_cast<const V8<T>*>(krow + ks * 16 + g * 8);
+      vf[ks] = *reinterpret_cast<const V8<T>*>(vrow + ks * 16 + g * 8);
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
     }
   };
   auto store_rows = [&](int buf) {
-    half_t* base = smem + buf * BUF;
+    T* base = smem + buf * BUF;
     if constexpr (SWZ) {
       tile_store_swz<BM, NT>(qr, base);
       tile_store_swz<BM, NT>(dr, base + TR);
@@ -351,10 +354,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     const int q0 = qstart + t * BM;
     const int buf = t & 1;
-    const half_t* Qr = smem + buf * BUF;
-    const half_t* Dr = Qr + TR;
-    const half_t* Qt = SWZ ? Qr : Qr + 2 * TR;
-    const half_t* Dt = SWZ ? Dr : Qt + TT;
+    const T* Qr = smem + buf * BUF;
+    const T* Dr = Qr + TR;
+    const T* Qt = SWZ ? Qr : Qr + 2 * TR;
+    const T* Dt = SWZ ? Dr : Qt + TT;
     const float* Ls = lsd[buf][0];
     const float* Dl = lsd[buf][1];
     __syncthreads();
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
       if (CAUSAL && qs + 31 < kw) continue;  // every query of the block precedes every key
       // Row-wise operands first (S and dP do not depend on each other), then the
       // transposed operands of dV and dK, so LDS latency overlaps the MFMAs.
-      h8 qf[8], of[8];
+      V8<T> qf[8], of[8];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         qf[ks] = SWZ ? frag_r_swz(Qr, qb * 32, ks * 2) : frag_r(Qr, qb * 32, ks * 2);
@@ -375,10 +378,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
         of[ks] = SWZ ? frag_r_swz(Dr, qb * 32, ks * 2) : frag_r(Dr, qb * 32, ks * 2);
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s = mma(qf[ks], kf[ks], s);
+      for (int ks = 0; ks < 8; ++ks) s = Mfma<T>::mma(qf[ks], kf[ks], s);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) dp = mma(of[ks], vf[ks], dp);
-      h8 dt[2][4], qt[2][4];
+      for (int ks = 0; ks < 8; ++ks) dp = Mfma<T>::mma(of[ks], vf[ks], dp);
+      V8<T> dt[2][4], qt[2][4];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -415,45 +418,45 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const h8 pf = cvt8(p, tt);
+        const V8<T> pf = cvt8<T>(p, tt);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dv[db] = mma(dt[tt][db], pf, dv[db]);
+        for (int db = 0; db < 4; ++db) dv[db] = Mfma<T>::mma(dt[tt][db], pf, dv[db]);
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const h8 sf = cvt8(ds, tt);
+        const V8<T> sf = cvt8<T>(ds, tt);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dk[db] = mma(qt[tt][db], sf, dk[db]);
+        for (int db = 0; db < 4; ++db) dk[db] = Mfma<T>::mma(qt[tt][db], sf, dk[db]);
       }
     }
     if (more) store_rows(buf ^ 1);
   }
 
   if (kj < a.Sk) {
-    half_t* dkrow = (half_t*)a.dk.p + b * a.dk.sb + h * a.dk.sh + (int64_t)kj * a.dk.ss;
-    half_t* dvrow = (half_t*)a.dv.p + b * a.dv.sb + h * a.dv.sh + (int64_t)kj * a.dv.ss;
+    T* dkrow = (T*)a.dk.p + b * a.dk.sb + h * a.dk.sh + (int64_t)kj * a.dk.ss;
+    T* dvrow = (T*)a.dv.p + b * a.dv.sb + h * a.dv.sh + (int64_t)kj * a.dv.ss;
     store_row4x4(dkrow, dk, a.scale, g);
     store_row4x4(dvrow, dv, 1.f, g);
   }
 }
 
-template <int BN, int NW, bool CAUSAL, bool SWZ>
+template <class T, int BN, int NW, bool CAUSAL, bool SWZ>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
   constexpr int BM = 32 * NW;
   const int64_t grid = (((int64_t)a.Sq + BM - 1) / BM) * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_f16_d128<BN, NW, CAUSAL, SWZ>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_f16_d128<T, BN, NW, CAUSAL, SWZ>),
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
 }
 
-template <int BM, int NW, bool CAUSAL, bool SWZ>
+template <class T, int BM, int NW, bool CAUSAL, bool SWZ>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
   constexpr int BN = 32 * NW;
   const int64_t grid = (((int64_t)a.Sk + BN - 1) / BN) * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_f16_d128<BM, NW, CAUSAL, SWZ>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_f16_d128<T, BM, NW, CAUSAL, SWZ>),
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
 }
 
@@ -468,15 +471,20 @@ TileCfg dq_fast_cfg(int v) {
   const int row_halfs = v >= 3 ? 2 * kD : 2 * kLSR + kLST;
   return TileCfg{32 * nw, bn, nw, 2 * bn * row_halfs * 2};
 }
-hipError_t launch_dq_fast(const BwdArgs& a, int v, int causal, hipStream_t s) {
+template <class T>
+hipError_t launch_dq_variant(const BwdArgs& a, int v, int causal, hipStream_t s) {
   switch (v) {
-    case 0: return causal ? launch_dq_t<64, 8, true, false>(a, s) : launch_dq_t<64, 8, false, false>(a, s);
-    case 1: return causal ? launch_dq_t<64, 4, true, false>(a, s) : launch_dq_t<64, 4, false, false>(a, s);
-    case 2: return causal ? launch_dq_t<32, 8, true, false>(a, s) : launch_dq_t<32, 8, false, false>(a, s);
-    case 3: return causal ? launch_dq_t<32, 8, true, true>(a, s) : launch_dq_t<32, 8, false, true>(a, s);
-    case 4: return causal ? launch_dq_t<64, 8, true, true>(a, s) : launch_dq_t<64, 8, false, true>(a, s);
+    case 0: return causal ? launch_dq_t<T, 64, 8, true, false>(a, s) : launch_dq_t<T, 64, 8, false, false>(a, s);
+    case 1: return causal ? launch_dq_t<T, 64, 4, true, false>(a, s) : launch_dq_t<T, 64, 4, false, false>(a, s);
+    case 2: return causal ? launch_dq_t<T, 32, 8, true, false>(a, s) : launch_dq_t<T, 32, 8, false, false>(a, s);
+    case 3: return causal ? launch_dq_t<T, 32, 8, true, true>(a, s) : launch_dq_t<T, 32, 8, false, true>(a, s);
+    case 4: return causal ? launch_dq_t<T, 64, 8, true, true>(a, s) : launch_dq_t<T, 64, 8, false, true>(a, s);
   }
   return hipErrorInvalidValue;
+}
+hipError_t launch_dq_fast(const BwdArgs& a, int v, int dtype, int causal, hipStream_t s) {
+  if (dtype == 2) return launch_dq_variant<bf16_t>(a, v, causal, s);
+  return launch_dq_variant<half_t>(a, v, causal, s);
 }
 
 // dK/dV variants: 0 = (BM 64, 4 waves), 1 = (BM 32, 4 waves), 2 = (BM 64,
@@ -489,14 +497,19 @@ TileCfg dkdv_fast_cfg(int v) {
   const int row_halfs = v >= 2 ? 2 * kD : 2 * kLSR + 2 * kLST;
   return TileCfg{bm, 32 * nw, nw, 2 * bm * row_halfs * 2 + 2 * 2 * bm * 4};
 }
-hipError_t launch_dkdv_fast(const BwdArgs& a, int v, int causal, hipStream_t s) {
+template <class T>
+hipError_t launch_dkdv_variant(const BwdArgs& a, int v, int causal, hipStream_t s) {
   switch (v) {
-    case 0: return causal ? launch_dkdv_t<64, 4, true, false>(a, s) : launch_dkdv_t<64, 4, false, false>(a, s);
-    case 1: return causal ? launch_dkdv_t<32, 4, true, false>(a, s) : launch_dkdv_t<32, 4, false, false>(a, s);
-    case 2: return causal ? launch_dkdv_t<64, 4, true, true>(a, s) : launch_dkdv_t<64, 4, false, true>(a, s);
-    case 3: return causal ? launch_dkdv_t<128, 4, true, true>(a, s) : launch_dkdv_t<128, 4, false, true>(a, s);
+    case 0: return causal ? launch_dkdv_t<T, 64, 4, true, false>(a, s) : launch_dkdv_t<T, 64, 4, false, false>(a, s);
+    case 1: return causal ? launch_dkdv_t<T, 32, 4, true, false>(a, s) : launch_dkdv_t<T, 32, 4, false, false>(a, s);
+    case 2: return causal ? launch_dkdv_t<T, 64, 4, true, true>(a, s) : launch_dkdv_t<T, 64, 4, false, true>(a, s);
+    case 3: return causal ? launch_dkdv_t<T, 128, 4, true, true>(a, s) : launch_dkdv_t<T, 128, 4, false, true>(a, s);
   }
   return hipErrorInvalidValue;
+}
+hipError_t launch_dkdv_fast(const BwdArgs& a, int v, int dtype, int causal, hipStream_t s) {
+  if (dtype == 2) return launch_dkdv_variant<bf16_t>(a, v, causal, s);
+  return launch_dkdv_variant<half_t>(a, v, causal, s);
 }
 
 }  // namespace fa

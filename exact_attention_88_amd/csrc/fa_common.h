@@ -7,8 +7,8 @@
 //   B (K x 32):  lane holds B[g*KPL + e][c]
 //   C (32 x 32): lane holds, in register r, C[crow(r, g)][c]
 //                with crow(r, g) = (r/4)*8 + g*4 + r%4
-// KPL = 8, K = 16 for v_mfma_f32_32x32x16_f16 and KPL = 1, K = 2 for the
-// full-precision v_mfma_f32_32x32x2f32.
+// KPL = 8, K = 16 for v_mfma_f32_32x32x16_f16 and v_mfma_f32_32x32x16_bf16,
+// and KPL = 1, K = 2 for the full-precision v_mfma_f32_32x32x2f32.
 //
 // The accumulator layout puts one column (a fixed query or key) in each lane
 // and spreads the other index over registers.  Feeding a C tile back as the
@@ -24,8 +24,11 @@
 namespace fa {
 
 typedef _Float16 half_t;
-typedef half_t h8 __attribute__((ext_vector_type(8)));
-typedef half_t h4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16_t;
+template <class T> using V8 = T __attribute__((ext_vector_type(8)));
+template <class T> using V4 = T __attribute__((ext_vector_type(4)));
+typedef V8<half_t> h8;
+typedef V4<half_t> h4;
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -41,6 +44,15 @@ template <> struct Mfma<half_t> {
   typedef h8 frag;
   static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<bf16_t> {
+  static constexpr int KPL = 8;
+  static constexpr int KSTEP = 16;
+  typedef V8<bf16_t> frag;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
 };
 
@@ -131,9 +143,9 @@ __device__ __forceinline__ void load_row_frags(typename Mfma<T>::frag* f, const 
     const int col = ks * M::KSTEP + g * M::KPL;
     if constexpr (sizeof(T) == 2) {
       if (vec) {
-        f[ks] = *reinterpret_cast<const h8*>(src + col);
+        f[ks] = *reinterpret_cast<const typename M::frag*>(src + col);
       } else {
-        h8 t;
+        typename M::frag t;
 #pragma unroll
         for (int e = 0; e < 8; ++e) t[e] = src[(int64_t)(col + e) * sd];
         f[ks] = t;
@@ -151,7 +163,7 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_rows(const T* lds, int rb
   const int lane = threadIdx.x & 63, g = lane >> 5, c = lane & 31;
   const T* p = lds + (rbase + c) * LS + cbase + g * Mfma<T>::KPL;
   if constexpr (sizeof(T) == 2) {
-    return *reinterpret_cast<const h8*>(p);
+    return *reinterpret_cast<const typename Mfma<T>::frag*>(p);
   } else {
     return *p;
   }
@@ -212,12 +224,12 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_tr(const T* lds, int rbas
     const int col = cbase + ((lane >> 4) & 1) * 16 + (j & 3) * 4;
     const int row = rbase + t * 16 + g * 4 + (j >> 2);
     typedef __attribute__((address_space(3))) s4 lds_s4;
-    const half_t* p0 = lds + row * LS + col;
-    const half_t* p1 = p0 + 8 * LS;
+    const T* p0 = lds + row * LS + col;
+    const T* p1 = p0 + 8 * LS;
     s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
     s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1));
-    h4 ah = __builtin_bit_cast(h4, a), bh = __builtin_bit_cast(h4, b);
-    h8 r;
+    V4<T> ah = __builtin_bit_cast(V4<T>, a), bh = __builtin_bit_cast(V4<T>, b);
+    typename Mfma<T>::frag r;
     r[0] = ah[0]; r[1] = ah[1]; r[2] = ah[2]; r[3] = ah[3];
     r[4] = bh[0]; r[5] = bh[1]; r[6] = bh[2]; r[7] = bh[3];
     return r;
@@ -232,9 +244,9 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_tr(const T* lds, int rbas
 template <class T>
 __device__ __forceinline__ typename Mfma<T>::frag frag_from_acc(const f32x16& acc, int t) {
   if constexpr (sizeof(T) == 2) {
-    h8 r;
+    typename Mfma<T>::frag r;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (half_t)acc[t * 8 + e];
+    for (int e = 0; e < 8; ++e) r[e] = (T)acc[t * 8 + e];
     return r;
   } else {
     return acc[t];
@@ -249,9 +261,9 @@ __device__ __forceinline__ void store4(T* __restrict__ rowp, int64_t sd, int col
   if (col >= D) return;
   if constexpr (sizeof(T) == 2) {
     if (vec) {
-      h4 h;
-      h[0] = (half_t)v[0]; h[1] = (half_t)v[1]; h[2] = (half_t)v[2]; h[3] = (half_t)v[3];
-      *reinterpret_cast<h4*>(rowp + col) = h;
+      V4<T> h;
+      h[0] = (T)v[0]; h[1] = (T)v[1]; h[2] = (T)v[2]; h[3] = (T)v[3];
+      *reinterpret_cast<V4<T>*>(rowp + col) = h;
       return;
     }
   } else {

@@ -209,14 +209,14 @@ constexpr int count_for(int dt, int D) { return count_ok(dt, D); }
 
 // fp16 with head dim 128 puts the tuned kernel's variants (fa_fwd_f16.hip)
 // first in its table; the generic entries follow.
-static int fast_count(int dtype, int D) { return (dtype == 0 && D == 128) ? fwd_fast_variants() : 0; }
+static int fast_count(int dtype, int D) { return (table_dt(dtype) == 0 && D == 128) ? fwd_fast_variants() : 0; }
 
 static int generic_count(int dtype, int D) {
   switch (D) {
-    case 16: return count_for(dtype, 16);
-    case 32: return count_for(dtype, 32);
-    case 64: return count_for(dtype, 64);
-    case 128: return count_for(dtype, 128);
+    case 16: return count_for(table_dt(dtype), 16);
+    case 32: return count_for(table_dt(dtype), 32);
+    case 64: return count_for(table_dt(dtype), 64);
+    case 128: return count_for(table_dt(dtype), 128);
   }
   return 0;
 }
@@ -225,10 +225,10 @@ int fwd_tile_count(int dtype, int D) { return fast_count(dtype, D) + generic_cou
 
 static int raw_for(int dtype, int D, int id) {
   switch (D) {
-    case 16: return raw_index(dtype, 16, id);
-    case 32: return raw_index(dtype, 32, id);
-    case 64: return raw_index(dtype, 64, id);
-    case 128: return raw_index(dtype, 128, id);
+    case 16: return raw_index(table_dt(dtype), 16, id);
+    case 32: return raw_index(table_dt(dtype), 32, id);
+    case 64: return raw_index(table_dt(dtype), 64, id);
+    case 128: return raw_index(table_dt(dtype), 128, id);
   }
   return -1;
 }
@@ -242,8 +242,8 @@ const TileCfg* fwd_tile(int dtype, int D, int id) {
     return &cfg;
   }
   const int raw = raw_for(dtype, D, id - nf);
-  const FwdTile t = tile_at(dtype, raw);
-  cfg = TileCfg{32 * t.nw, t.bn, t.nw, lds_bytes(dtype == 0 ? 2 : 4, D, t.bn)};
+  const FwdTile t = tile_at(table_dt(dtype), raw);
+  cfg = TileCfg{32 * t.nw, t.bn, t.nw, lds_bytes(elem_size(dtype), D, t.bn)};
   return &cfg;
 }
 
@@ -252,7 +252,7 @@ int fwd_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
   // measured fastest on MI355X at S = 4096 and 16384, causal and not (by
   // 1-3 % over the plain 8-wave kernel).
   (void)Sq; (void)Sk; (void)causal;
-  if (dtype == 0 && D == 128) return 0;
+  if (table_dt(dtype) == 0 && D == 128) return 0;
   return 0;
 }
 
@@ -262,7 +262,7 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, int causal, int tile, 
     // The tuned kernel needs 16-byte vector access to q, k, v and out; other
     // layouts run the generic kernel's first entry instead.
     const int need = VEC_Q | VEC_K | VEC_V | VEC_O;
-    if ((a.vec & need) == need) return launch_fwd_fast(a, tile, causal, s);
+    if ((a.vec & need) == need) return launch_fwd_fast(a, tile, dtype, causal, s);
     tile = nf;
   }
   const int raw = raw_for(dtype, D, tile - nf);
@@ -273,6 +273,13 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, int causal, int tile, 
       case 32: return dispatch<half_t, 32>(a, raw, causal, s);
       case 64: return dispatch<half_t, 64>(a, raw, causal, s);
       case 128: return dispatch<half_t, 128>(a, raw, causal, s);
+    }
+  } else if (dtype == 2) {
+    switch (D) {
+      case 16: return dispatch<bf16_t, 16>(a, raw, causal, s);
+      case 32: return dispatch<bf16_t, 32>(a, raw, causal, s);
+      case 64: return dispatch<bf16_t, 64>(a, raw, causal, s);
+      case 128: return dispatch<bf16_t, 128>(a, raw, causal, s);
     }
   } else {
     switch (D) {

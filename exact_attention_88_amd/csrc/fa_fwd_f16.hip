@@ -1,4 +1,5 @@
-// Forward attention for fp16 with head dim 128 on gfx950: the tuned path.
+// Forward attention for 16-bit inputs (fp16, bf16) with head dim 128 on
+// gfx950: the tuned path.
 //
 // Same method as the generic forward kernel ("FlashAttention-2 from PyTorch to
 // Triton": online softmax over streamed K/V tiles, one program per query tile;
@@ -46,8 +47,8 @@ __device__ __forceinline__ int xcd_logical_block() {
 // Global -> register staging of a ROWS x 128 fp16 tile (16-byte chunks,
 // PER per thread) and register -> padded LDS store.  Native vector types keep
 // the staging in VGPRs.
-template <int ROWS, int NT>
-__device__ __forceinline__ void tile_load(u32x4* r, const half_t* __restrict__ base, int64_t ss,
+template <int ROWS, int NT, class T>
+__device__ __forceinline__ void tile_load(u32x4* r, const T* __restrict__ base, int64_t ss,
                                           int row0, int nrows) {
   constexpr int PER = ROWS * 16 / NT;
 #pragma unroll
@@ -58,8 +59,8 @@ __device__ __forceinline__ void tile_load(u32x4* r, const half_t* __restrict__ b
   }
 }
 
-template <int ROWS, int NT, int LS>
-__device__ __forceinline__ void tile_store(const u32x4* r, half_t* lds) {
+template <int ROWS, int NT, int LS, class T>
+__device__ __forceinline__ void tile_store(const u32x4* r, T* lds) {
   constexpr int PER = ROWS * 16 / NT;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -70,34 +71,36 @@ __device__ __forceinline__ void tile_store(const u32x4* r, half_t* lds) {
 
 // Row-wise operand fragment of the K tile: lane (c, g) gets row rbase + c,
 // chunk kchunk + g.
-__device__ __forceinline__ h8 frag_rows_k(const half_t* lds, int rbase, int kchunk) {
+template <class T>
+__device__ __forceinline__ V8<T> frag_rows_k(const T* lds, int rbase, int kchunk) {
   const int lane = threadIdx.x & 63;
-  return *reinterpret_cast<const h8*>(lds + (rbase + (lane & 31)) * kLSK +
+  return *reinterpret_cast<const V8<T>*>(lds + (rbase + (lane & 31)) * kLSK +
                                       (kchunk + (lane >> 5)) * 8);
 }
 
 // Transposed operand fragment (see frag_tr in fa_common.h) of the V tile.
-__device__ __forceinline__ h8 frag_tr_v(const half_t* lds, int rbase, int t, int cbase) {
+template <class T>
+__device__ __forceinline__ V8<T> frag_tr_v(const T* lds, int rbase, int t, int cbase) {
   const int lane = threadIdx.x & 63, g = lane >> 5, j = lane & 15;
   const int col = cbase + ((lane >> 4) & 1) * 16 + (j & 3) * 4;
   const int row = rbase + t * 16 + g * 4 + (j >> 2);
   typedef __attribute__((address_space(3))) s4 lds_s4;
-  const half_t* p0 = lds + row * kLSV + col;
+  const T* p0 = lds + row * kLSV + col;
   s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
   s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + 8 * kLSV));
-  h4 ah = __builtin_bit_cast(h4, a), bh = __builtin_bit_cast(h4, b);
-  h8 r;
+  V4<T> ah = __builtin_bit_cast(V4<T>, a), bh = __builtin_bit_cast(V4<T>, b);
+  V8<T> r;
   r[0] = ah[0]; r[1] = ah[1]; r[2] = ah[2]; r[3] = ah[3];
   r[4] = bh[0]; r[5] = bh[1]; r[6] = bh[2]; r[7] = bh[3];
   return r;
 }
 
-template <int BN, int NW, bool CAUSAL>
+template <class T, int BN, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
   constexpr int BM = 32 * NW, NT = NW * 64;
   constexpr int NKB = BN / 32;
   constexpr int TK = BN * kLSK, TV = BN * kLSV;
-  __shared__ __attribute__((aligned(1024))) half_t smem[2 * TK + 2 * TV];  // K0 K1 V0 V1
+  __shared__ __attribute__((aligned(1024))) T smem[2 * TK + 2 * TV];  // K0 K1 V0 V1
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nqb = (a.Sq + BM - 1) / BM;
@@ -106,17 +109,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
   const int bh = L / nqb;
   if (CAUSAL) qb = nqb - 1 - qb;
   const int b = bh / a.H, h = bh % a.H;
-  const half_t* qbase = (const half_t*)a.q.p + b * a.q.sb + h * a.q.sh;
-  const half_t* kbase = (const half_t*)a.k.p + b * a.k.sb + h * a.k.sh;
-  const half_t* vbase = (const half_t*)a.v.p + b * a.v.sb + h * a.v.sh;
+  const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
+  const T* kbase = (const T*)a.k.p + b * a.k.sb + h * a.k.sh;
+  const T* vbase = (const T*)a.v.p + b * a.v.sb + h * a.v.sh;
 
   const int q0 = qb * BM, qw = q0 + w * 32, qi = qw + c;
 
-  h8 qf[8];
+  V8<T> qf[8];
   {
-    const half_t* qrow = qbase + (int64_t)min(qi, a.Sq - 1) * a.q.ss;
+    const T* qrow = qbase + (int64_t)min(qi, a.Sq - 1) * a.q.ss;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const h8*>(qrow + ks * 16 + g * 8);
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const V8<T>*>(qrow + ks * 16 + g * 8);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): Q is resident before the tile loop
 
@@ -139,8 +142,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BN;
     const int buf = t & 1;
-    const half_t* Ks = smem + buf * TK;
-    const half_t* Vs = smem + 2 * TK + buf * TV;
+    const T* Ks = smem + buf * TK;
+    const T* Vs = smem + 2 * TK + buf * TV;
     __syncthreads();
     const bool more = t + 1 < ntiles;
     if (more) {
@@ -151,13 +154,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
       f32x16 s[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        h8 kf[8];
+        V8<T> kf[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) kf[ks] = frag_rows_k(Ks, kb * 32, ks * 2);
         s[kb] = zero16();
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], s[kb], 0, 0, 0);
+          s[kb] = Mfma<T>::mma(kf[ks], qf[ks], s[kb]);
       }
       if ((k0 + BN > a.Sk) || (CAUSAL && k0 + BN - 1 > qw)) {
 #pragma unroll
@@ -200,15 +203,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          h8 vf[4];
+          V8<T> vf[4];
 #pragma unroll
           for (int db = 0; db < 4; ++db) vf[db] = frag_tr_v(Vs, kb * 32, tt, db * 32);
-          h8 pf;
+          V8<T> pf;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pf[e] = (half_t)s[kb][tt * 8 + e];
+          for (int e = 0; e < 8; ++e) pf[e] = (T)s[kb][tt * 8 + e];
 #pragma unroll
           for (int db = 0; db < 4; ++db)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pf, oacc[db], 0, 0, 0);
+            oacc[db] = Mfma<T>::mma(vf[db], pf, oacc[db]);
         }
     }
     if (more) {
@@ -220,15 +223,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
   const float ltot = lsum + xor32(lsum);
   if (qi < a.Sq) {
     const float inv = 1.f / ltot;
-    half_t* orow = (half_t*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
+    T* orow = (T*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        h4 o4;
+        V4<T> o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (half_t)(oacc[db][r4 * 4 + e] * inv);
-        *reinterpret_cast<h4*>(orow + db * 32 + r4 * 8 + g * 4) = o4;
+        for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[db][r4 * 4 + e] * inv);
+        *reinterpret_cast<V4<T>*>(orow + db * 32 + r4 * 8 + g * 4) = o4;
       }
     if (g == 0)
       a.lse[(int64_t)bh * a.Sq + qi] = __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2);
@@ -247,17 +250,17 @@ __device__ __forceinline__ float add_xor32(float x) {
 }
 
 // Scores of one tile for one wave without scheduling constraints.
-template <int NKB>
-__device__ __forceinline__ void scores_free(f32x16* s, const half_t* Ks, const h8* qf) {
+template <int NKB, class T>
+__device__ __forceinline__ void scores_free(f32x16* s, const T* Ks, const V8<T>* qf) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    h8 kf[8];
+    V8<T> kf[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kf[ks] = frag_rows_k(Ks, kb * 32, ks * 2);
     s[kb] = zero16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], s[kb], 0, 0, 0);
+      s[kb] = Mfma<T>::mma(kf[ks], qf[ks], s[kb]);
   }
 }
 
@@ -267,10 +270,10 @@ __device__ __forceinline__ void scores_free(f32x16* s, const half_t* Ks, const h
 // land.  The sched_barrier fences pin that order and let only VALU, SALU and
 // global loads (the softmax of the previous tile, address arithmetic) move
 // across, into the gaps.
-template <int NKB>
-__device__ __forceinline__ void scores_ordered(f32x16* s, const half_t* Ks, const h8* qf) {
+template <int NKB, class T>
+__device__ __forceinline__ void scores_ordered(f32x16* s, const T* Ks, const V8<T>* qf) {
   constexpr int kFloat = 0x2 | 0x4 | 0x20;  // VALU, SALU, VMEM read
-  h8 kf[2][8];
+  V8<T> kf[2][8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) kf[0][ks] = frag_rows_k(Ks, 0, ks * 2);
   __builtin_amdgcn_sched_barrier(kFloat);
@@ -279,7 +282,7 @@ __device__ __forceinline__ void scores_ordered(f32x16* s, const half_t* Ks, cons
     s[kb] = zero16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kb & 1][ks], qf[ks], s[kb], 0, 0, 0);
+      s[kb] = Mfma<T>::mma(kf[kb & 1][ks], qf[ks], s[kb]);
       if (kb + 1 < NKB) kf[(kb + 1) & 1][ks] = frag_rows_k(Ks, (kb + 1) * 32, ks * 2);
       __builtin_amdgcn_sched_barrier(kFloat);
     }
@@ -289,23 +292,23 @@ __device__ __forceinline__ void scores_ordered(f32x16* s, const half_t* Ks, cons
 // O^T += V^T P^T for one tile with the same pinned order: the transposed V
 // fragments of the first 16-key step are read up front, and each MFMA is
 // followed by the reads of one fragment of the next step.
-template <int NKB>
-__device__ __forceinline__ void pv_ordered(f32x16* oacc, const half_t* Vs, const f32x16* p,
-                                           const h8* vf0) {
+template <int NKB, class T>
+__device__ __forceinline__ void pv_ordered(f32x16* oacc, const T* Vs, const f32x16* p,
+                                           const V8<T>* vf0) {
   constexpr int kFloat = 0x2 | 0x4 | 0x20 | 0x200;  // VALU, SALU, VMEM read, DS write
   constexpr int NS = NKB * 2;                       // 16-key steps per tile
-  h8 vf[2][4];
+  V8<T> vf[2][4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) vf[0][db] = vf0[db];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     const int kb = st >> 1, tt = st & 1;
-    h8 pf;
+    V8<T> pf;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pf[e] = (half_t)p[kb][tt * 8 + e];
+    for (int e = 0; e < 8; ++e) pf[e] = (T)p[kb][tt * 8 + e];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[st & 1][db], pf, oacc[db], 0, 0, 0);
+      oacc[db] = Mfma<T>::mma(vf[st & 1][db], pf, oacc[db]);
       if (st + 1 < NS)
         vf[(st + 1) & 1][db] = frag_tr_v(Vs, ((st + 1) >> 1) * 32, (st + 1) & 1, db * 32);
       __builtin_amdgcn_sched_barrier(kFloat);
@@ -332,12 +335,12 @@ constexpr float kLazy = 8.f;
 // taken, and the half-wave max and sum use a VALU lane swap.
 // ORDERED pins the read/MFMA order (scores_ordered, pv_ordered) and reads the
 // first V fragments before the scores.
-template <int BN, int NW, bool CAUSAL, bool ORDERED>
+template <class T, int BN, int NW, bool CAUSAL, bool ORDERED>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
   constexpr int BM = 32 * NW, NT = NW * 64;
   constexpr int NKB = BN / 32;
   constexpr int TK = BN * kLSK, TV = BN * kLSV;
-  __shared__ __attribute__((aligned(1024))) half_t smem[2 * TK + 2 * TV];  // K0 K1 V0 V1
+  __shared__ __attribute__((aligned(1024))) T smem[2 * TK + 2 * TV];  // K0 K1 V0 V1
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nqb = (a.Sq + BM - 1) / BM;
@@ -346,17 +349,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
   const int bh = L / nqb;
   if (CAUSAL) qb = nqb - 1 - qb;
   const int b = bh / a.H, h = bh % a.H;
-  const half_t* qbase = (const half_t*)a.q.p + b * a.q.sb + h * a.q.sh;
-  const half_t* kbase = (const half_t*)a.k.p + b * a.k.sb + h * a.k.sh;
-  const half_t* vbase = (const half_t*)a.v.p + b * a.v.sb + h * a.v.sh;
+  const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
+  const T* kbase = (const T*)a.k.p + b * a.k.sb + h * a.k.sh;
+  const T* vbase = (const T*)a.v.p + b * a.v.sb + h * a.v.sh;
 
   const int q0 = qb * BM, qi = q0 + w * 32 + c;
 
-  h8 qf[8];
+  V8<T> qf[8];
   {
-    const half_t* qrow = qbase + (int64_t)min(qi, a.Sq - 1) * a.q.ss;
+    const T* qrow = qbase + (int64_t)min(qi, a.Sq - 1) * a.q.ss;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const h8*>(qrow + ks * 16 + g * 8);
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const V8<T>*>(qrow + ks * 16 + g * 8);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): Q is resident before the tile loop
 
@@ -398,9 +401,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
     tile_load<BN, NT>(kr, kbase, a.k.ss, k0 + 2 * BN, a.Sk);
     tile_load<BN, NT>(vr, vbase, a.v.ss, k0 + BN, a.Sk);
     f32x16 snxt[NKB];
-    const half_t* Vs = smem + 2 * TK + (t & 1) * TV;
-    const half_t* Kn = smem + ((t + 1) & 1) * TK;
-    h8 vf0[4];
+    const T* Vs = smem + 2 * TK + (t & 1) * TV;
+    const T* Kn = smem + ((t + 1) & 1) * TK;
+    V8<T> vf0[4];
     if constexpr (ORDERED) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) vf0[db] = frag_tr_v(Vs, 0, 0, db * 32);
@@ -454,15 +457,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          h8 vf[4];
+          V8<T> vf[4];
 #pragma unroll
           for (int db = 0; db < 4; ++db) vf[db] = frag_tr_v(Vs, kb * 32, tt, db * 32);
-          h8 pf;
+          V8<T> pf;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pf[e] = (half_t)scur[kb][tt * 8 + e];
+          for (int e = 0; e < 8; ++e) pf[e] = (T)scur[kb][tt * 8 + e];
 #pragma unroll
           for (int db = 0; db < 4; ++db)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pf, oacc[db], 0, 0, 0);
+            oacc[db] = Mfma<T>::mma(vf[db], pf, oacc[db]);
         }
     }
     tile_store<BN, NT, kLSK>(kr, smem + (t & 1) * TK);
@@ -478,15 +481,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
   const float ltot = add_xor32(lsum);
   if (qi < a.Sq) {
     const float inv = 1.f / ltot;
-    half_t* orow = (half_t*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
+    T* orow = (T*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        h4 o4;
+        V4<T> o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (half_t)(oacc[db][r4 * 4 + e] * inv);
-        *reinterpret_cast<h4*>(orow + db * 32 + r4 * 8 + g * 4) = o4;
+        for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[db][r4 * 4 + e] * inv);
+        *reinterpret_cast<V4<T>*>(orow + db * 32 + r4 * 8 + g * 4) = o4;
       }
     if (g == 0)
       a.lse[(int64_t)bh * a.Sq + qi] = __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2);
@@ -502,16 +505,27 @@ hipError_t launch_k(Kernel* k, int BM, int threads, const FwdArgs& a, hipStream_
                          args, 0, s);
 }
 
-template <int BN, int NW, bool ORDERED>
+template <class T, int BN, int NW, bool ORDERED>
 hipError_t launch_pipe(const FwdArgs& a, int causal, hipStream_t s) {
-  return causal ? launch_k(&fwd_f16_d128_pipe<BN, NW, true, ORDERED>, 32 * NW, NW * 64, a, s)
-                : launch_k(&fwd_f16_d128_pipe<BN, NW, false, ORDERED>, 32 * NW, NW * 64, a, s);
+  return causal ? launch_k(&fwd_f16_d128_pipe<T, BN, NW, true, ORDERED>, 32 * NW, NW * 64, a, s)
+                : launch_k(&fwd_f16_d128_pipe<T, BN, NW, false, ORDERED>, 32 * NW, NW * 64, a, s);
 }
 
-template <int BN, int NW>
+template <class T, int BN, int NW>
 hipError_t launch_plain(const FwdArgs& a, int causal, hipStream_t s) {
-  return causal ? launch_k(&fwd_f16_d128<BN, NW, true>, 32 * NW, NW * 64, a, s)
-                : launch_k(&fwd_f16_d128<BN, NW, false>, 32 * NW, NW * 64, a, s);
+  return causal ? launch_k(&fwd_f16_d128<T, BN, NW, true>, 32 * NW, NW * 64, a, s)
+                : launch_k(&fwd_f16_d128<T, BN, NW, false>, 32 * NW, NW * 64, a, s);
+}
+
+template <class T>
+hipError_t launch_variant(const FwdArgs& a, int variant, int causal, hipStream_t s) {
+  switch (variant) {
+    case 0: return launch_pipe<T, 64, 8, true>(a, causal, s);
+    case 1: return launch_pipe<T, 64, 8, false>(a, causal, s);
+    case 2: return launch_plain<T, 64, 8>(a, causal, s);
+    case 3: return launch_plain<T, 64, 4>(a, causal, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -525,14 +539,9 @@ TileCfg fwd_fast_cfg(int v) {
   return TileCfg{32 * nw, 64, nw, 2 * 64 * (kLSK + kLSV) * 2};
 }
 
-hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int causal, hipStream_t s) {
-  switch (variant) {
-    case 0: return launch_pipe<64, 8, true>(a, causal, s);
-    case 1: return launch_pipe<64, 8, false>(a, causal, s);
-    case 2: return launch_plain<64, 8>(a, causal, s);
-    case 3: return launch_plain<64, 4>(a, causal, s);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int dtype, int causal, hipStream_t s) {
+  if (dtype == 2) return launch_variant<bf16_t>(a, variant, causal, s);
+  return launch_variant<half_t>(a, variant, causal, s);
 }
 
 }  // namespace fa

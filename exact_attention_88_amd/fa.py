@@ -17,10 +17,10 @@ __all__ = ["FAError", "fa_fwd", "fa_bwd", "fa_fwd_tile", "fa_bwd_tile", "fa_bwd_
            "fa_tile_count",
            "fa_tile_info", "fa_tile_default", "fa_status_string", "fa_last_hip_error", "fa_version",
            "lib_path",
-           "FA_F16", "FA_F32", "FA_PASS_FWD", "FA_PASS_BWD_DKDV", "FA_PASS_BWD_DQ",
+           "FA_F16", "FA_F32", "FA_BF16", "FA_PASS_FWD", "FA_PASS_BWD_DKDV", "FA_PASS_BWD_DQ",
            "EXPORTED_SYMBOLS"]
 
-FA_F16, FA_F32 = 0, 1
+FA_F16, FA_F32, FA_BF16 = 0, 1, 2
 FA_PASS_FWD, FA_PASS_BWD_DKDV, FA_PASS_BWD_DQ = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_fwd_tile", "fa_bwd_tile", "fa_bwd_stage",
@@ -145,7 +145,9 @@ def _dtype_code(t):
         return FA_F16
     if t.dtype == torch.float32:
         return FA_F32
-    raise TypeError(f"unsupported dtype {t.dtype}; fa supports float16 and float32")
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; fa supports float16, bfloat16 and float32")
 
 
 def _stream_ptr(t):

@@ -7,7 +7,9 @@ method.
 
 Every tensor is standard-normal, drawn with ``numpy.random.default_rng(seed)``
 in float32 in the order q, k, v, dO, and rounded to float16 (round to nearest
-even, numpy's cast) when the case is half precision.  The pages benchmark and
+even, numpy's cast) when the case is half precision, or to the nearest
+bfloat16 value (ties to even; kept in a float32 array, which holds every
+bfloat16 value exactly) when the case is bfloat16.  The pages benchmark and
 test on ``randn`` inputs of this kind ("FlashAttention-2 from PyTorch to
 Triton", the benchmark harness and the test file), so no dataset is involved.
 """
@@ -19,7 +21,7 @@ import math
 import numpy as np
 
 __all__ = ["Case", "make_inputs", "CONFIGS", "tiny_case", "sweep_cases", "edge_cases",
-           "long_case", "mid_case", "scale_for"]
+           "long_case", "mid_case", "scale_for", "round_to_bf16", "bf16_cases"]
 
 
 @dataclass(frozen=True)
@@ -38,7 +40,7 @@ class Case:
     Sq: int
     Sk: int
     D: int
-    dtype: str            # "f16" or "f32"
+    dtype: str            # "f16", "bf16" or "f32"
     causal: bool
     seed: int
     layout: str = "bhsd"
@@ -46,6 +48,7 @@ class Case:
 
     @property
     def np_dtype(self):
+        """Host storage type: float16, or float32 (for f32 and for bf16 values)."""
         return np.float16 if self.dtype == "f16" else np.float32
 
     @property
@@ -58,10 +61,21 @@ def scale_for(D: int) -> float:
     return float(np.float32(1.0 / math.sqrt(D)))
 
 
-def _draw(rng, shape, dtype, mult=1.0):
+def round_to_bf16(x):
+    """float32 array -> float32 array of the nearest bfloat16 values (ties to
+    even): the upper 16 bits of the float32 pattern after rounding the lower
+    16.  Finite inputs only (these are normal draws)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).reshape(np.shape(x))
+
+
+def _draw(rng, shape, dtype, mult=1.0, bf16=False):
     x = rng.standard_normal(shape, dtype=np.float32)
     if mult != 1.0:
         x = x * np.float32(mult)
+    if bf16:
+        return round_to_bf16(x)
     return x.astype(dtype)
 
 
@@ -80,10 +94,11 @@ def make_inputs(case: Case, with_grad: bool = True):
     for name in names:
         S = case.Sq if name in ("q", "do") else case.Sk
         mult = case.q_mult if name == "q" else 1.0
+        bf16 = case.dtype == "bf16"
         if case.layout == "bhsd":
-            out[name] = _draw(rng, (case.B, case.H, S, case.D), dt, mult)
+            out[name] = _draw(rng, (case.B, case.H, S, case.D), dt, mult, bf16)
         elif case.layout == "bshd":
-            store = _draw(rng, (case.B, S, case.H, case.D), dt, mult)
+            store = _draw(rng, (case.B, S, case.H, case.D), dt, mult, bf16)
             out[name] = store.transpose(0, 2, 1, 3)
         else:
             raise ValueError(f"unknown layout {case.layout}")
@@ -123,6 +138,22 @@ def edge_cases():
         cases.append(Case(f"edge_peaked_{dtype}_c_D128_S1537", 2, 4, 1537, 1537, 128, dtype,
                           True, seed=30 + idx, layout="bshd", q_mult=8.0))
         idx += 1
+    return cases
+
+
+def bf16_cases():
+    """bfloat16 cases (the fp16 families' shapes): ragged strided [B,S,H,D]
+    storage at D in {16, 64, 128}, causal and not, plus the peaked-softmax case
+    (Q x 8) at D=128.  Seeds 60..."""
+    cases = []
+    idx = 0
+    for causal in (False, True):
+        for D, S in ((16, 1000), (64, 777), (128, 1000)):
+            cases.append(Case(f"bf16_{'c' if causal else 'nc'}_D{D}_S{S}", 2, 4, S, S, D, "bf16",
+                              causal, seed=60 + idx, layout="bshd"))
+            idx += 1
+    cases.append(Case("bf16_peaked_c_D128_S1537", 2, 4, 1537, 1537, 128, "bf16", True,
+                      seed=60 + idx, layout="bshd", q_mult=8.0))
     return cases
 
 

@@ -52,7 +52,9 @@ extern "C" {
 
 typedef enum {
   FA_F16 = 0, /* IEEE binary16 storage, fp16 MFMA with fp32 accumulation */
-  FA_F32 = 1  /* IEEE binary32 storage, full-precision fp32 MFMA (no reduced-precision xf32) */
+  FA_F32 = 1, /* IEEE binary32 storage, full-precision fp32 MFMA (no reduced-precision xf32) */
+  FA_BF16 = 2 /* bfloat16 storage, bf16 MFMA with fp32 accumulation; P and dS are rounded to
+                 bfloat16 (nearest even) before their products, as P is for fp16 */
 } fa_dtype;
 
 typedef enum {

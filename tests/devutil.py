@@ -5,7 +5,11 @@ Tolerances (the pages' own ones existed only because of TF32, so the bars here
 are tighter):
   float32: max |x - ref| <= 2e-5 for O and LSE, <= 1e-4 for dQ, dK, dV;
   float16: max |x - ref| / max |ref| <= 2e-3 for O and <= 1e-2 for dQ, dK, dV,
-           and max |lse - ref| <= 2e-3 (LSE is float32 from float32 sums).
+           and max |lse - ref| <= 2e-3 (LSE is float32 from float32 sums);
+  bfloat16: the float16 bars scaled by the ratio of the unit roundoffs
+           (2^-8 against 2^-11: the errors come from rounding P, dS and the
+           outputs to the 16-bit type), 1.6e-2 for O and 8e-2 for the
+           gradients, relative to max |ref|; LSE as for float16.
 """
 from __future__ import annotations
 
@@ -14,22 +18,28 @@ import numpy as np
 TOL = {
     "f32": {"o": 2e-5, "lse": 2e-5, "grad": 1e-4},
     "f16": {"o": 2e-3, "lse": 2e-3, "grad": 1e-2},
+    "bf16": {"o": 1.6e-2, "lse": 2e-3, "grad": 8e-2},
 }
 
 
 def torch_dtype(case_dtype):
     import torch
-    return torch.float16 if case_dtype == "f16" else torch.float32
+    return {"f16": torch.float16, "bf16": torch.bfloat16}.get(case_dtype, torch.float32)
 
 
-def to_device(x, device="cuda"):
+def to_device(x, device="cuda", dtype=None):
     """numpy [B,H,S,D] (possibly a transposed view of [B,S,H,D]) -> torch view
-    with the same logical shape and the same storage order on the device."""
+    with the same logical shape and the same storage order on the device,
+    converted to ``dtype`` if given (exact for bfloat16-valued float32 input)."""
     import torch
     if x.flags["C_CONTIGUOUS"]:
-        return torch.from_numpy(np.array(x)).to(device)
+        t = torch.from_numpy(np.array(x)).to(device)
+        return t if dtype is None else t.to(dtype)
     store = np.ascontiguousarray(x.transpose(0, 2, 1, 3))
-    return torch.from_numpy(store).to(device).transpose(1, 2)
+    t = torch.from_numpy(store).to(device)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.transpose(1, 2)
 
 
 def empty_like_layout(shape, dtype, layout, device="cuda", fill=float("nan")):
@@ -52,9 +62,9 @@ def host(t):
 
 def err(x, ref, dtype, kind):
     """Error measure for this dtype and quantity (absolute for f32 and LSE,
-    relative to max |ref| for f16 tensors)."""
+    relative to max |ref| for 16-bit tensors)."""
     d = float(np.max(np.abs(x - ref))) if x.size else 0.0
-    if dtype == "f16" and kind != "lse":
+    if dtype in ("f16", "bf16") and kind != "lse":
         m = float(np.max(np.abs(ref))) if ref.size else 0.0
         return d / m if m > 0 else d
     return d

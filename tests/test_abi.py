@@ -138,7 +138,7 @@ def test_bwd_validation():
     assert _bwd(tiles=(0, m)) == -7
 
 
-@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("dtype", [0, 1, 2])
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
 def test_tile_tables_fit_lds_and_are_consistent(dtype, D):
     for p in (fa.FA_PASS_FWD, fa.FA_PASS_BWD_DKDV, fa.FA_PASS_BWD_DQ):

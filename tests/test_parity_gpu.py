@@ -27,8 +27,8 @@ def run_case(case, tiles=(-1, -1, -1), layout_out=None, x=None):
     generator unless ``x`` is given); returns the inputs and host results."""
     fa = _fa()
     x = W.make_inputs(case) if x is None else x
-    dq_t = {n: U.to_device(a) for n, a in x.items()}
     tdt = U.torch_dtype(case.dtype)
+    dq_t = {n: U.to_device(a, dtype=tdt) for n, a in x.items()}
     lay = layout_out or case.layout
     B, H, Sq, Sk, D = case.B, case.H, case.Sq, case.Sk, case.D
     o = U.empty_like_layout((B, H, Sq, D), tdt, lay)
@@ -65,7 +65,7 @@ def check_full(case, x, got):
           flush=True)
     for name in ref:
         assert errs[name] <= U.tol(case.dtype, name), (case.name, name, errs[name])
-    assert errs["delta"] <= (1e-5 if case.dtype == "f32" else 2e-3)
+    assert errs["delta"] <= {"f32": 1e-5, "f16": 2e-3, "bf16": 1.6e-2}[case.dtype]
     return errs
 
 
@@ -114,12 +114,13 @@ def _rising_inputs(case, growth):
     x = W.make_inputs(case)
     ramp = (1.0 + growth * np.arange(case.Sk) / max(1, case.Sk - 1)).astype(np.float64)
     k = x["k"].astype(np.float64) * ramp[None, None, :, None]
-    x["k"] = k.astype(x["k"].dtype)
+    x["k"] = W.round_to_bf16(k.astype(np.float32)) if case.dtype == "bf16" else k.astype(x["k"].dtype)
     return x
 
 
-RISING = [(dname, D, causal, t) for dname, D in (("f16", 128), ("f16", 64), ("f32", 64))
-          for causal in (False, True) for t in range(4 if (dname, D) == ("f16", 128) else 1)]
+RISING = [(dname, D, causal, t) for dname, D in (("f16", 128), ("bf16", 128), ("f16", 64),
+                                                 ("f32", 64))
+          for causal in (False, True) for t in range(4 if D == 128 and dname != "f32" else 1)]
 
 
 @pytest.mark.parametrize("dname,D,causal,t", RISING,
@@ -131,8 +132,14 @@ def test_rising_scores_rescale(dname, D, causal, t):
     case = W.Case(f"rising_{dname}_D{D}_{causal}", 1, 2, 700, 700, D, dname, causal,
                   seed=300 + D, q_mult=4.0)
     fa = _fa()
-    nf = fa.fa_tile_count(fa.FA_PASS_FWD, 0 if dname == "f16" else 1, D)
+    nf = fa.fa_tile_count(fa.FA_PASS_FWD, {"f16": 0, "f32": 1, "bf16": 2}[dname], D)
     x, got = run_case(case, tiles=(t % nf, -1, -1), x=_rising_inputs(case, 3.0))
+    check_full(case, x, got)
+
+
+@pytest.mark.parametrize("case", W.bf16_cases(), ids=lambda c: c.name)
+def test_bf16_cases(case):
+    x, got = run_case(case)
     check_full(case, x, got)
 
 
@@ -167,7 +174,7 @@ def test_deterministic_bitwise():
 def _tile_cases():
     fa = _fa()
     out = []
-    for dtype, dname in ((0, "f16"), (1, "f32")):
+    for dtype, dname in ((0, "f16"), (1, "f32"), (2, "bf16")):
         for D in (16, 32, 64, 128):
             nf = fa.fa_tile_count(fa.FA_PASS_FWD, dtype, D)
             nkv = fa.fa_tile_count(fa.FA_PASS_BWD_DKDV, dtype, D)
