@@ -99,6 +99,28 @@ def time_path(fa, torch, case, dev, steps, warmup):
     return wall, avg
 
 
+def peak_memory(torch, case, dev):
+    """Peak device memory of one forward + backward through the autograd entry
+    point, beyond the inputs: the four outputs (O, dQ, dK, dV) plus what the
+    method keeps per query row (LSE, and the rowsum workspace)."""
+    from exact_attention_88_amd.autograd import attention
+    q, k, v = (dev[n].detach().clone().requires_grad_(True) for n in ("q", "k", "v"))
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    o = attention(q, k, v, causal=case.causal, scale=case.scale)
+    o.backward(dev["do"])
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    rows = case.B * case.H * case.Sq
+    outputs = (2 * rows + 2 * case.B * case.H * case.Sk) * case.D * q.element_size()
+    del o, q, k, v
+    return {"peak_beyond_inputs_bytes": int(peak), "outputs_bytes": int(outputs),
+            "beyond_outputs_bytes": int(peak - outputs),
+            "beyond_outputs_bytes_per_query_row": round((peak - outputs) / rows, 2),
+            "materialised_fp32_scores_bytes": int(rows * case.Sk * 4)}
+
+
 def library_source_sha():
     import glob
     import hashlib
@@ -226,6 +248,7 @@ def main():
                         "ms_per_step": round(bwall / bsteps * 1e3, 4), "steps": bsteps,
                         "kernel_ms": {n: round(v, 4) for n, v in bavg.items()}}
         del bdev
+    line["memory"] = peak_memory(torch, case, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, x, args.cpu_heads)
     if args.sweep:

@@ -167,9 +167,25 @@ def _check(st):
 
 
 def _check_4d(*ts):
+    """Every tensor handed to the kernels is a 4-d tensor in device memory on
+    one GPU: a host pointer reaching a kernel would be a memory fault, not an
+    error code, so it is refused here."""
+    dev = None
     for t in ts:
         if t.dim() != 4:
             raise ValueError("fa expects [B, H, S, D] tensors")
+        if not t.is_cuda:
+            raise ValueError("fa runs on the GPU only: every tensor must be in device memory")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("fa expects all tensors on the same device")
+
+
+def _check_same_device(ref, *ts):
+    for t in ts:
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError("fa expects all tensors on the same GPU")
 
 
 def fa_fwd_tile(tile_id, q, k, v, causal=False, scale=None, out=None, lse=None):
@@ -190,6 +206,8 @@ def fa_fwd_tile(tile_id, q, k, v, causal=False, scale=None, out=None, lse=None):
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [B, H, Sq]")
+    _check_4d(q, k, v, out)
+    _check_same_device(q, lse)
     st = _lib.fa_fwd_tile(int(tile_id), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                           _strides(v), B, H, Sq, Sk, D, int(bool(causal)), float(scale),
                           _dtype_code(q), _ptr(out), _strides(out), _ptr(lse), _stream_ptr(q))
@@ -225,6 +243,8 @@ def fa_bwd_tile(dkdv_tile, dq_tile, q, k, v, o, dout, lse, causal=False, scale=N
     for t in (lse, delta):
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError("lse and delta must be contiguous float32 [B, H, Sq]")
+    _check_4d(q, k, v, o, dout, dq, dk, dv)
+    _check_same_device(q, lse, delta)
     args = (_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(o),
             _strides(o), _ptr(dout), _strides(dout), _ptr(lse), B, H, Sq, Sk, D,
             int(bool(causal)), float(scale), _dtype_code(q), _ptr(delta), _ptr(dq), _strides(dq),
