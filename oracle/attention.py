@@ -13,13 +13,19 @@ oracle is that plain definition, written out with the full score matrix, in
 float64, one (batch, head) at a time:
 
     S   = s * Q K^T                      (s = the float32 scale, widened)
-    S_ij = -inf  for j > i  when causal  (top-left aligned lower triangle,
-                                          the ``tril`` reference of the same
-                                          page's test file)
+    S_ij = -inf  for j > i + c  when causal
+                                         (c = 0: top-left aligned lower
+                                          triangle, the ``tril`` reference of
+                                          the same page's test file; c = Sk - Sq:
+                                          bottom-right aligned, ``causal=2``)
     LSE_i = log sum_j exp(S_ij)          (the per-row log-sum-exp L that the
                                           page stores for the backward)
     P   = exp(S - LSE)
     O   = P V
+
+A row with no visible key (bottom-right alignment with Sq > Sk; the page
+leaves such rows to later work) is defined to give LSE = -inf, P = 0, O = 0
+and no gradient.
 
 and its gradient, by the chain rule through the softmax (the page's backward
 outline names dO, the saved L and rowsum(dO o O)):
@@ -45,7 +51,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["attention_forward", "attention_backward", "delta_rowsum", "head_forward",
-           "head_backward", "head_forward_rows", "head_backward_rows"]
+           "head_backward", "head_forward_rows", "head_backward_rows", "causal_offset"]
 
 ROW_BLOCK = 2048
 
@@ -54,33 +60,55 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _scores(q, k, scale, causal, r0):
+def causal_offset(causal, Sq, Sk):
+    """Key index of the last key query 0 sees (queries see keys j <= i + c):
+    None when not causal, 0 for top-left alignment (causal True or 1), Sk - Sq
+    for bottom-right alignment (causal == 2)."""
+    if not causal:
+        return None
+    return Sk - Sq if int(causal) == 2 else 0
+
+
+def _mask(s, q_rows, k_cols, off):
+    """Apply the causal mask to s[len(q_rows), len(k_cols)] (absolute indices)."""
+    if off is None:
+        return s
+    return np.where(np.asarray(k_cols)[None, :] > np.asarray(q_rows)[:, None] + off, -np.inf, s)
+
+
+def _scores(q, k, scale, off, r0):
     """Scaled scores for query rows r0.. of one head, causal mask applied."""
     s = scale * (q @ k.T)
-    if causal:
-        rows = np.arange(r0, r0 + q.shape[0])[:, None]
-        cols = np.arange(k.shape[0])[None, :]
-        s = np.where(cols > rows, -np.inf, s)
-    return s
+    return _mask(s, np.arange(r0, r0 + q.shape[0]), np.arange(k.shape[0]), off)
 
 
 def _lse(s):
-    """log sum_j exp(s_ij) for each row, shifted by the row max for range."""
+    """log sum_j exp(s_ij) for each row, shifted by the row max for range;
+    -inf for a row whose every score is masked."""
     m = s.max(axis=1, keepdims=True)
-    return m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
+    m = np.where(np.isneginf(m), 0.0, m)
+    with np.errstate(divide="ignore"):
+        return m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
+
+
+def _probs(s, L):
+    """P = exp(S - LSE), and 0 on rows with no visible key."""
+    with np.errstate(invalid="ignore"):
+        return np.where(np.isneginf(L), 0.0, np.exp(s - L))
 
 
 def head_forward(q, k, v, scale, causal, row_block=ROW_BLOCK):
     """One head: q [Sq,D], k [Sk,D], v [Sk,D] -> (o [Sq,D], lse [Sq])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     Sq = q.shape[0]
+    off = causal_offset(causal, Sq, k.shape[0])
     o = np.empty((Sq, v.shape[1]))
     lse = np.empty(Sq)
     for r0 in range(0, Sq, row_block):
         r1 = min(Sq, r0 + row_block)
-        s = _scores(q[r0:r1], k, scale, causal, r0)
+        s = _scores(q[r0:r1], k, scale, off, r0)
         L = _lse(s)
-        p = np.exp(s - L)
+        p = _probs(s, L)
         o[r0:r1] = p @ v
         lse[r0:r1] = L[:, 0]
     return o, lse
@@ -90,13 +118,14 @@ def head_backward(q, k, v, do, scale, causal, row_block=ROW_BLOCK):
     """One head: gradients (dq, dk, dv) of <dO, O(q, k, v)>."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     Sq = q.shape[0]
+    off = causal_offset(causal, Sq, k.shape[0])
     dq = np.empty_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for r0 in range(0, Sq, row_block):
         r1 = min(Sq, r0 + row_block)
-        s = _scores(q[r0:r1], k, scale, causal, r0)
-        p = np.exp(s - _lse(s))
+        s = _scores(q[r0:r1], k, scale, off, r0)
+        p = _probs(s, _lse(s))
         dv += p.T @ do[r0:r1]
         dp = do[r0:r1] @ v.T
         ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
@@ -140,11 +169,10 @@ def head_forward_rows(q, k, v, scale, causal, rows):
     plain definition over its full score row): (o [len(rows), D], lse [len(rows)])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     rows = np.asarray(rows, dtype=np.int64)
-    s = scale * (q[rows] @ k.T)
-    if causal:
-        s = np.where(np.arange(k.shape[0])[None, :] > rows[:, None], -np.inf, s)
+    off = causal_offset(causal, q.shape[0], k.shape[0])
+    s = _mask(scale * (q[rows] @ k.T), rows, np.arange(k.shape[0]), off)
     L = _lse(s)
-    return np.exp(s - L) @ v, L[:, 0]
+    return _probs(s, L) @ v, L[:, 0]
 
 
 def head_backward_rows(q, k, v, do, scale, causal, q_rows, k_rows, row_block=ROW_BLOCK):
@@ -157,29 +185,26 @@ def head_backward_rows(q, k, v, do, scale, causal, q_rows, k_rows, row_block=ROW
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     Sq = q.shape[0]
+    off = causal_offset(causal, Sq, k.shape[0])
     lse = np.empty(Sq)
     psum = np.empty(Sq)
     for r0 in range(0, Sq, row_block):
         r1 = min(Sq, r0 + row_block)
-        s = _scores(q[r0:r1], k, scale, causal, r0)
+        s = _scores(q[r0:r1], k, scale, off, r0)
         L = _lse(s)
-        p = np.exp(s - L)
+        p = _probs(s, L)
         psum[r0:r1] = (p * (do[r0:r1] @ v.T)).sum(axis=1)
         lse[r0:r1] = L[:, 0]
     q_rows = np.asarray(q_rows, dtype=np.int64)
     k_rows = np.asarray(k_rows, dtype=np.int64)
     # dq rows: full key range for each sampled query.
-    s = scale * (q[q_rows] @ k.T)
-    if causal:
-        s = np.where(np.arange(k.shape[0])[None, :] > q_rows[:, None], -np.inf, s)
-    p = np.exp(s - lse[q_rows][:, None])
+    s = _mask(scale * (q[q_rows] @ k.T), q_rows, np.arange(k.shape[0]), off)
+    p = _probs(s, lse[q_rows][:, None])
     ds = p * (do[q_rows] @ v.T - psum[q_rows][:, None])
     dq = scale * (ds @ k)
     # dk, dv rows: full query range for each sampled key (columns of P).
-    s = scale * (q @ k[k_rows].T)
-    if causal:
-        s = np.where(k_rows[None, :] > np.arange(Sq)[:, None], -np.inf, s)
-    p = np.exp(s - lse[:, None])
+    s = _mask(scale * (q @ k[k_rows].T), np.arange(Sq), k_rows, off)
+    p = _probs(s, lse[:, None])
     dv = p.T @ do
     ds = p * (do @ v[k_rows].T - psum[:, None])
     dk = scale * (ds.T @ q)
