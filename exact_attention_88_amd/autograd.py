@@ -35,13 +35,14 @@ class _Attention(torch.autograd.Function):
         return dq, dk, dv, None, None
 
 
-def attention(q, k, v, causal: bool = False, scale: float | None = None):
+def attention(q, k, v, causal=False, scale: float | None = None):
     """Exact scaled-dot-product attention of ``[B, H, S, D]`` tensors (any
     strides; fp16, bf16 or fp32 on one GPU), differentiable once.
 
-    ``scale`` defaults to ``1/sqrt(D)``; ``causal`` keeps key j for query i
-    iff j <= i (top-left aligned when Sq != Sk).
+    ``scale`` defaults to ``1/sqrt(D)``; ``causal`` is False (none), True or
+    1 (key j visible to query i iff j <= i, top-left aligned), or 2 /
+    "bottom_right" (j <= i + Sk - Sq; rows with no visible key give 0).
     """
     if scale is None:
         scale = q.shape[-1] ** -0.5
-    return _Attention.apply(q, k, v, bool(causal), float(scale))
+    return _Attention.apply(q, k, v, causal, float(scale))

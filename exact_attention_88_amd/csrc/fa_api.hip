@@ -59,6 +59,7 @@ int fwd_impl(int tile, const void* q, const int64_t* qs, const void* k, const in
              float* lse, void* stream) {
   int st = shape_check(B, H, Sq, Sk, D, dtype);
   if (st != FA_OK) return st;
+  if (causal < 0 || causal > 2) return FA_ERR_CAUSAL;
   if (B * H * Sq == 0) return FA_OK;
   if (!q || !k || !v || !out || !lse) return FA_ERR_NULL;
   if (!qs || !ks || !vs || !os) return FA_ERR_NULL;
@@ -86,6 +87,7 @@ int fwd_impl(int tile, const void* q, const int64_t* qs, const void* k, const in
   a.scale_log2 = scale * 1.4426950408889634f;
   a.vec = (vec_ok(q, qs, es) ? fa::VEC_Q : 0) | (vec_ok(k, ks, es) ? fa::VEC_K : 0) |
           (vec_ok(v, vs, es) ? fa::VEC_V : 0) | (vec_ok(out, os, es) ? fa::VEC_O : 0);
+  a.coff = causal == 2 ? (int)(Sk - Sq) : 0;
   return hip_status(fa::launch_fwd(a, dt, d, causal ? 1 : 0, tile, (hipStream_t)stream));
 }
 
@@ -98,6 +100,7 @@ int bwd_impl(int stage, int tile_kv, int tile_q, const void* q, const int64_t* q
              void* dv, const int64_t* dvs, void* stream) {
   int st = shape_check(B, H, Sq, Sk, D, dtype);
   if (st != FA_OK) return st;
+  if (causal < 0 || causal > 2) return FA_ERR_CAUSAL;
   if (B * H == 0 || (Sq == 0 && Sk == 0)) return FA_OK;
   const bool has_q = Sq > 0;
   if (!k || !v || !dk || !dv || !ks || !vs || !dks || !dvs) return FA_ERR_NULL;
@@ -149,6 +152,7 @@ int bwd_impl(int stage, int tile_kv, int tile_q, const void* q, const int64_t* q
     vec |= (vec_ok(q, qs, es) ? fa::VEC_Q : 0) | (vec_ok(o, os, es) ? fa::VEC_O : 0) |
            (vec_ok(dout, dos, es) ? fa::VEC_DO : 0) | (vec_ok(dq, dqs, es) ? fa::VEC_DQ : 0);
   a.vec = vec;
+  a.coff = causal == 2 ? (int)(Sk - Sq) : 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (has_q && (stage < 0 || stage == 0)) e = fa::launch_bwd_pre(a, dt, d, s);
@@ -272,6 +276,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output aliases an input or another output";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error at launch";
     case FA_ERR_TILE: return "FA_ERR_TILE: tile id out of range";
+    case FA_ERR_CAUSAL: return "FA_ERR_CAUSAL: causal must be 0, 1 (top-left) or 2 (bottom-right)";
   }
   return "unknown fa_status";
 }

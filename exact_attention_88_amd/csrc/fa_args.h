@@ -24,6 +24,7 @@ struct FwdArgs {
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   int vec;           // VEC_* bits: 16-byte vector access allowed per tensor
+  int coff;          // causal: query i sees keys j <= i + coff (0 top-left, Sk - Sq bottom-right)
 };
 
 struct BwdArgs {
@@ -34,6 +35,7 @@ struct BwdArgs {
   float scale;       // softmax scale (applied to dq, dk)
   float scale_log2;  // scale * log2(e)
   int vec;
+  int coff;          // causal: query i sees keys j <= i + coff (0 top-left, Sk - Sq bottom-right)
 };
 
 struct TileCfg {

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
   const bool vecq = a.vec & VEC_Q, vecd = a.vec & VEC_DO;
   const bool key_tail = k0 + BN > a.Sk;
 
-  const int qstart = CAUSAL ? (k0 / BM) * BM : 0;
+  const int qstart = CAUSAL ? (max(0, k0 - a.coff) / BM) * BM : 0;
   for (int q0 = qstart; q0 < a.Sq; q0 += BM) {
     __syncthreads();
     load_tile<T, BM, D, LS, NT>(Qs, qbase, a.q.ss, a.q.sd, q0, a.Sq, vecq);
@@ -146,16 +146,18 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
     for (int r = threadIdx.x; r < BM; r += NT) {
       const int i = q0 + r;
       // fp16 kernels use LSE*log2(e); fp32 kernels use LSE itself.
-      Ls[r] = i < a.Sq ? (sizeof(T) == 2 ? lse[i] * kLog2e : lse[i]) : INFINITY;
+      // Rows past the end, and rows with no visible key (LSE = -inf), get P = 0.
+      const float li = i < a.Sq ? lse[i] : INFINITY;
+      Ls[r] = li == -INFINITY ? INFINITY : (sizeof(T) == 2 ? li * kLog2e : li);
       Dl[r] = i < a.Sq ? dl[i] : 0.f;
     }
     __syncthreads();
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qs = q0 + qb * 32;
-      if (CAUSAL && qs + 31 < kw) continue;  // every query of the block precedes every key
+      if (CAUSAL && qs + a.coff + 31 < kw) continue;  // every query of the block precedes every key
       f32x16 s = dot_block<T, D, LS>(Qs, qb * 32, kf);
-      const bool need_mask = key_tail || (CAUSAL && qs < kw + 31);
+      const bool need_mask = key_tail || (CAUSAL && qs + a.coff < kw + 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qr = qb * 32 + crow(r, g);
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
           p = fast_exp2(__builtin_fmaf(s[r], cs, -Ls[qr]));
         else
           p = fast_exp2(__builtin_fmaf(a.scale, s[r], -Ls[qr]) * kLog2e);
-        if (need_mask && (kj >= a.Sk || (CAUSAL && kj > q0 + qr))) p = 0.f;
+        if (need_mask && (kj >= a.Sk || (CAUSAL && kj > q0 + qr + a.coff))) p = 0.f;
         s[r] = p;
       }
 #pragma unroll

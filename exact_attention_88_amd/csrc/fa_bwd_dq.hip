@@ -85,7 +85,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
   load_row_frags<T, D>(df, dobase, a.dout.ss, a.dout.sd, qi, a.Sq, a.vec & VEC_DO);
   const bool valid = qi < a.Sq;
   // fp16 uses LSE*log2(e) in one FMA per score; fp32 uses LSE itself (see below).
-  const float lse_n = valid ? a.lse[(int64_t)bh * a.Sq + qi] : INFINITY;
+  // Rows past the end, and rows with no visible key (LSE = -inf), get P = 0.
+  float lse_n = valid ? a.lse[(int64_t)bh * a.Sq + qi] : INFINITY;
+  if (lse_n == -INFINITY) lse_n = INFINITY;
   const float lse2 = sizeof(T) == 2 ? lse_n * kLog2e : lse_n;
   const float dlt = valid ? a.delta[(int64_t)bh * a.Sq + qi] : 0.f;
 
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
   const float cs = a.scale_log2;
   const bool veck = a.vec & VEC_K, vecv = a.vec & VEC_V;
 
-  const int kend = CAUSAL ? min(a.Sk, q0 + BM) : a.Sk;
+  const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
   const int ntiles = (kend + BN - 1) / BN;
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BN;
@@ -106,9 +108,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int ks0 = k0 + kb * 32;
-      if (CAUSAL && ks0 > qw + 31) continue;  // block entirely after this wave's rows
+      if (CAUSAL && ks0 > qw + a.coff + 31) continue;  // block entirely after this wave's rows
       f32x16 s = dot_block<T, D, LS>(Ks, kb * 32, qf);
-      const bool need_mask = (ks0 + 32 > a.Sk) || (CAUSAL && ks0 + 31 > qw);
+      const bool need_mask = (ks0 + 32 > a.Sk) || (CAUSAL && ks0 + 31 > qw + a.coff);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = ks0 + crow(r, g);
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
           p = fast_exp2(__builtin_fmaf(s[r], cs, -lse2));
         else
           p = fast_exp2(__builtin_fmaf(a.scale, s[r], -lse2) * kLog2e);
-        if (need_mask && (key >= a.Sk || (CAUSAL && key > qi))) p = 0.f;
+        if (need_mask && (key >= a.Sk || (CAUSAL && key > qi + a.coff))) p = 0.f;
         s[r] = p;
       }
       const f32x16 dp = dot_block<T, D, LS>(Vs, kb * 32, df);

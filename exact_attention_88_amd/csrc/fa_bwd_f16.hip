@@ -186,7 +186,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
       df[ks] = *reinterpret_cast<const V8<T>*>(drow + ks * 16 + g * 8);
     }
   }
-  const float lse2 = valid ? a.lse[(int64_t)bh * a.Sq + qi] * kLog2e : INFINITY;
+  // Rows past the end, and rows with no visible key (LSE = -inf), get P = 0.
+  const float lse_n = valid ? a.lse[(int64_t)bh * a.Sq + qi] : INFINITY;
+  const float lse2 = lse_n == -INFINITY ? INFINITY : lse_n * kLog2e;
   const float dlt = valid ? a.delta[(int64_t)bh * a.Sq + qi] : 0.f;
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): row data resident before the tile loop
 
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
   for (int i = 0; i < 4; ++i) dq[i] = zero16();
   const float cs = a.scale_log2;
 
-  const int kend = CAUSAL ? min(a.Sk, q0 + BM) : a.Sk;
+  const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
   const int ntiles = (kend + BN - 1) / BN;
   constexpr int PER = BN * 16 / NT;
   u32x4 kr[PER], vr[PER];
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int ks0 = k0 + kb * 32;
-      if (CAUSAL && ks0 > qw + 31) continue;
+      if (CAUSAL && ks0 > qw + a.coff + 31) continue;
       // Row-wise operands of S^T and dP^T first, then the transposed K operand
       // of dQ (one k-step at a time: with 8 waves a wave has 256 registers).
       V8<T> kf[8], vf[8];
@@ -245,11 +247,11 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = fast_exp2(__builtin_fmaf(s[r], cs, -lse2));
       // Masks only on the diagonal block and the ragged key tail.
-      if ((ks0 + 32 > a.Sk) || (CAUSAL && ks0 + 31 > qw)) {
+      if ((ks0 + 32 > a.Sk) || (CAUSAL && ks0 + 31 > qw + a.coff)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = ks0 + crow(r, g);
-          if (key >= a.Sk || (CAUSAL && key > qi)) s[r] = 0.f;
+          if (key >= a.Sk || (CAUSAL && key > qi + a.coff)) s[r] = 0.f;
         }
       }
 #pragma unroll
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   const float cs = a.scale_log2;
   const bool key_tail = k0 + BN > a.Sk;
 
-  const int qstart = CAUSAL ? (k0 / BM) * BM : 0;
+  const int qstart = CAUSAL ? (max(0, k0 - a.coff) / BM) * BM : 0;
   const int ntiles = a.Sq > qstart ? (a.Sq - qstart + BM - 1) / BM : 0;
   constexpr int PER = BM * 16 / NT;
   u32x4 qr[PER], dr[PER];
@@ -326,7 +328,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
     tile_load<BM, NT>(dr, dobase, a.dout.ss, q0, a.Sq);
     if ((int)threadIdx.x < BM) {
       const int i = q0 + (int)threadIdx.x;
-      lsr = i < a.Sq ? lse[i] * kLog2e : INFINITY;
+      const float li = i < a.Sq ? lse[i] : INFINITY;  // LSE = -inf: no visible key, P = 0
+      lsr = li == -INFINITY ? INFINITY : li * kLog2e;
       dlr = i < a.Sq ? dl[i] : 0.f;
     }
   };
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qs = q0 + qb * 32;
-      if (CAUSAL && qs + 31 < kw) continue;  // every query of the block precedes every key
+      if (CAUSAL && qs + a.coff + 31 < kw) continue;  // every query of the block precedes every key
       // Row-wise operands first (S and dP do not depend on each other), then the
       // transposed operands of dV and dK, so LDS latency overlaps the MFMAs.
       V8<T> qf[8], of[8];
@@ -406,10 +409,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
         p[r] = fast_exp2(__builtin_fmaf(s[r], cs, -lr));
       }
       // Masks only on the diagonal block and the ragged key tail.
-      if (key_tail || (CAUSAL && qs < kw + 31)) {
+      if (key_tail || (CAUSAL && qs + a.coff < kw + 31)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kj >= a.Sk || (CAUSAL && kj > qs + crow(r, g))) p[r] = 0.f;
+          if (kj >= a.Sk || (CAUSAL && kj > qs + a.coff + crow(r, g))) p[r] = 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   float m = -INFINITY, lsum = 0.f;
   const float cs = a.scale_log2;
 
-  const int kend = CAUSAL ? min(a.Sk, q0 + BM) : a.Sk;
+  const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
   const int ntiles = (kend + BN - 1) / BN;
   const bool veck = a.vec & VEC_K, vecv = a.vec & VEC_V;
 
@@ -98,19 +98,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     load_tile<T, BN, D, LS, NT>(Ks, kbase, a.k.ss, a.k.sd, k0, a.Sk, veck);
     load_tile<T, BN, D, LS, NT>(Vs, vbase, a.v.ss, a.v.sd, k0, a.Sk, vecv);
     __syncthreads();
-    if (CAUSAL && k0 > qw + 31) continue;  // every key of the tile is after every row of this wave
+    if (CAUSAL && k0 > qw + a.coff + 31) continue;  // every key of the tile is after every row of this wave
 
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = dot_block<T, D, LS>(Ks, kb * 32, qf);
-    const bool need_mask = (k0 + BN > a.Sk) || (CAUSAL && k0 + BN - 1 > qw);
+    const bool need_mask = (k0 + BN > a.Sk) || (CAUSAL && k0 + BN - 1 > qw + a.coff);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + crow(r, g);
-          if (key >= a.Sk || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+          if (key >= a.Sk || (CAUSAL && key > qi + a.coff)) s[kb][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -158,7 +158,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 
   const float ltot = lsum + xor32(lsum);
   if (qi < a.Sq) {
-    const float inv = 1.f / ltot;
+    // A row with no visible key (bottom-right alignment, Sq > Sk) has
+    // ltot = 0: O = 0 and LSE = -inf.
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     T* orow = obase + (int64_t)qi * a.o.ss;
     const bool veco = a.vec & VEC_O;
 #pragma unroll
@@ -170,7 +172,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         for (int e = 0; e < 4; ++e) v4[e] = oacc[db][r4 * 4 + e] * inv;
         store4<T, D>(orow, a.o.sd, db * 32 + r4 * 8 + g * 4, v4, veco);
       }
-    if (g == 0) a.lse[(int64_t)bh * a.Sq + qi] = __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2);
+    if (g == 0)
+      a.lse[(int64_t)bh * a.Sq + qi] =
+          ltot > 0.f ? __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2) : -INFINITY;
   }
 }
 

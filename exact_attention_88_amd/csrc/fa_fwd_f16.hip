@@ -129,7 +129,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
   float m = -INFINITY, lsum = 0.f;
   const float cs = a.scale_log2;
 
-  const int kend = CAUSAL ? min(a.Sk, q0 + BM) : a.Sk;
+  const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
   const int ntiles = (kend + BN - 1) / BN;
 
   constexpr int PER = BN * 16 / NT;
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
       tile_load<BN, NT>(kr, kbase, a.k.ss, k0 + BN, a.Sk);
       tile_load<BN, NT>(vr, vbase, a.v.ss, k0 + BN, a.Sk);
     }
-    if (!(CAUSAL && k0 > qw + 31)) {
+    if (!(CAUSAL && k0 > qw + a.coff + 31)) {
       f32x16 s[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -162,13 +162,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
         for (int ks = 0; ks < 8; ++ks)
           s[kb] = Mfma<T>::mma(kf[ks], qf[ks], s[kb]);
       }
-      if ((k0 + BN > a.Sk) || (CAUSAL && k0 + BN - 1 > qw)) {
+      if ((k0 + BN > a.Sk) || (CAUSAL && k0 + BN - 1 > qw + a.coff)) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + crow(r, g);
-            if (key >= a.Sk || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+            if (key >= a.Sk || (CAUSAL && key > qi + a.coff)) s[kb][r] = -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
 
   const float ltot = lsum + xor32(lsum);
   if (qi < a.Sq) {
-    const float inv = 1.f / ltot;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;  // no visible key: O = 0, LSE = -inf
     T* orow = (T*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -234,7 +234,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
         *reinterpret_cast<V4<T>*>(orow + db * 32 + r4 * 8 + g * 4) = o4;
       }
     if (g == 0)
-      a.lse[(int64_t)bh * a.Sq + qi] = __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2);
+      a.lse[(int64_t)bh * a.Sq + qi] =
+          ltot > 0.f ? __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2) : -INFINITY;
   }
 }
 
@@ -369,13 +370,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
   float m = -INFINITY, lsum = 0.f;
   const float cs = a.scale_log2;
 
-  const int kend = CAUSAL ? min(a.Sk, q0 + BM) : a.Sk;
+  const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
   const int ntiles = (kend + BN - 1) / BN;
   // Tiles [0, nfull) hold no key past the end and, causally, no key after the
   // block's first query: no wave of the block masks them.  Every wave runs
   // every tile of its block: a tile entirely after a wave's rows is fully
   // masked (P = 0) and changes nothing.
-  const int nfull = min(ntiles, (CAUSAL ? min(a.Sk, q0 + 1) : a.Sk) / BN);
+  const int nfull = min(ntiles, (CAUSAL ? max(0, min(a.Sk, q0 + a.coff + 1)) : a.Sk) / BN);
 
   constexpr int PER = BN * 16 / NT;
   u32x4 kr[PER], vr[PER];
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + crow(r, g);
-          if (key >= a.Sk || (CAUSAL && key > qi)) scur[kb][r] = -INFINITY;
+          if (key >= a.Sk || (CAUSAL && key > qi + a.coff)) scur[kb][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
 
   const float ltot = add_xor32(lsum);
   if (qi < a.Sq) {
-    const float inv = 1.f / ltot;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;  // no visible key: O = 0, LSE = -inf
     T* orow = (T*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -492,7 +493,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
         *reinterpret_cast<V4<T>*>(orow + db * 32 + r4 * 8 + g * 4) = o4;
       }
     if (g == 0)
-      a.lse[(int64_t)bh * a.Sq + qi] = __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2);
+      a.lse[(int64_t)bh * a.Sq + qi] =
+          ltot > 0.f ? __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2) : -INFINITY;
   }
 }
 

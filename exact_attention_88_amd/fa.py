@@ -18,7 +18,7 @@ __all__ = ["FAError", "fa_fwd", "fa_bwd", "fa_fwd_tile", "fa_bwd_tile", "fa_bwd_
            "fa_tile_info", "fa_tile_default", "fa_status_string", "fa_last_hip_error", "fa_version",
            "lib_path",
            "FA_F16", "FA_F32", "FA_BF16", "FA_PASS_FWD", "FA_PASS_BWD_DKDV", "FA_PASS_BWD_DQ",
-           "EXPORTED_SYMBOLS"]
+           "CAUSAL_NONE", "CAUSAL_TOP_LEFT", "CAUSAL_BOTTOM_RIGHT", "EXPORTED_SYMBOLS"]
 
 FA_F16, FA_F32, FA_BF16 = 0, 1, 2
 FA_PASS_FWD, FA_PASS_BWD_DKDV, FA_PASS_BWD_DQ = 0, 1, 2
@@ -127,7 +127,7 @@ def fa_tile_info(pass_id: int, dtype: int, D: int, tile_id: int):
 
 
 def fa_tile_default(pass_id: int, dtype: int, D: int, Sq: int, Sk: int, causal: bool) -> int:
-    st = int(_lib.fa_tile_default(pass_id, dtype, D, Sq, Sk, int(bool(causal))))
+    st = int(_lib.fa_tile_default(pass_id, dtype, D, Sq, Sk, _causal_code(causal)))
     if st < 0:
         raise FAError(st)
     return st
@@ -182,6 +182,19 @@ def _check_4d(*ts):
             raise ValueError("fa expects all tensors on the same device")
 
 
+CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
+
+
+def _causal_code(causal):
+    """False/True map to 0/1 (none, top-left); the ints 0, 1, 2 and the
+    strings "top_left" / "bottom_right" are passed as the C ABI's codes."""
+    if isinstance(causal, str):
+        return {"none": 0, "top_left": 1, "bottom_right": 2}[causal]
+    if isinstance(causal, bool):
+        return int(causal)
+    return int(causal)
+
+
 def _check_same_device(ref, *ts):
     for t in ts:
         if not t.is_cuda or t.device != ref.device:
@@ -209,7 +222,7 @@ def fa_fwd_tile(tile_id, q, k, v, causal=False, scale=None, out=None, lse=None):
     _check_4d(q, k, v, out)
     _check_same_device(q, lse)
     st = _lib.fa_fwd_tile(int(tile_id), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
-                          _strides(v), B, H, Sq, Sk, D, int(bool(causal)), float(scale),
+                          _strides(v), B, H, Sq, Sk, D, _causal_code(causal), float(scale),
                           _dtype_code(q), _ptr(out), _strides(out), _ptr(lse), _stream_ptr(q))
     _check(st)
     return out, lse
@@ -247,7 +260,7 @@ def fa_bwd_tile(dkdv_tile, dq_tile, q, k, v, o, dout, lse, causal=False, scale=N
     _check_same_device(q, lse, delta)
     args = (_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(o),
             _strides(o), _ptr(dout), _strides(dout), _ptr(lse), B, H, Sq, Sk, D,
-            int(bool(causal)), float(scale), _dtype_code(q), _ptr(delta), _ptr(dq), _strides(dq),
+            _causal_code(causal), float(scale), _dtype_code(q), _ptr(delta), _ptr(dq), _strides(dq),
             _ptr(dk), _strides(dk), _ptr(dv), _strides(dv), _stream_ptr(q))
     if _stage is None:
         st = _lib.fa_bwd_tile(int(dkdv_tile), int(dq_tile), *args)

@@ -41,7 +41,7 @@ class Case:
     Sk: int
     D: int
     dtype: str            # "f16", "bf16" or "f32"
-    causal: bool
+    causal: int           # 0/False none, 1/True top-left, 2 bottom-right aligned
     seed: int
     layout: str = "bhsd"
     q_mult: float = 1.0

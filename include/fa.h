@@ -25,8 +25,13 @@
  * 64-bit arithmetic.  All device pointers must be device memory of the GPU
  * that is current when the call is made.
  *
- * Causal masking is top-left aligned: query row i sees keys 0..i (clipped to
- * Sk).  With Sk >= 1 every query row sees at least key 0.
+ * Causal masking (argument `causal`): 0 = none; 1 = top-left aligned, query
+ * row i sees keys 0..i (clipped to Sk), the pages' ``tril`` convention, so
+ * with Sk >= 1 every row sees key 0; 2 = bottom-right aligned, query row i
+ * sees keys 0..i + (Sk - Sq), the same as 1 when Sq == Sk.  Under 2 with
+ * Sq > Sk the first Sq - Sk rows see no key: their output row is 0, their
+ * lse is -inf and they contribute no gradient (the pages leave such rows
+ * open; this is the reading taken).  Other values are FA_ERR_CAUSAL.
  *
  * Ownership.  The caller owns every buffer.  The library allocates no device
  * memory and keeps no state other than read-only tables.  Outputs are fully
@@ -66,7 +71,8 @@ typedef enum {
   FA_ERR_STRIDE = -4, /* a negative stride */
   FA_ERR_ALIAS = -5,  /* an output base pointer equals an input's or another output's */
   FA_ERR_HIP = -6,    /* the HIP runtime reported an error at launch */
-  FA_ERR_TILE = -7    /* a forced tile id is out of range for this pass, dtype and D */
+  FA_ERR_TILE = -7,   /* a forced tile id is out of range for this pass, dtype and D */
+  FA_ERR_CAUSAL = -8  /* causal is not 0, 1 or 2 */
 } fa_status;
 
 /* Pass ids for the tile-table queries. */
@@ -77,7 +83,8 @@ typedef enum { FA_PASS_FWD = 0, FA_PASS_BWD_DKDV = 1, FA_PASS_BWD_DQ = 2 } fa_pa
  * the forward kernel and its online-softmax recurrence; "Triton
  * FlashAttention", the forward kernel description).
  *
- *   O[b,h,i,:] = sum_j softmax_j(scale * q_i . k_j) v_j   (j <= i when causal)
+ *   O[b,h,i,:] = sum_j softmax_j(scale * q_i . k_j) v_j   (j <= i + c when causal:
+ *                                                          c = 0, or Sk - Sq when causal = 2)
  *   lse[b,h,i] = log sum_j exp(scale * q_i . k_j)         (natural log, fp32)
  *
  * q: [B,H,Sq,D], k and v: [B,H,Sk,D], out: [B,H,Sq,D] (dtype), lse: [B,H,Sq]

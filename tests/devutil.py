@@ -63,7 +63,9 @@ def host(t):
 def err(x, ref, dtype, kind):
     """Error measure for this dtype and quantity (absolute for f32 and LSE,
     relative to max |ref| for 16-bit tensors)."""
-    d = float(np.max(np.abs(x - ref))) if x.size else 0.0
+    with np.errstate(invalid="ignore"):
+        diff = np.where(x == ref, 0.0, np.abs(x - ref))  # equal infinities (LSE = -inf) match
+    d = float(np.max(diff)) if x.size else 0.0
     if dtype in ("f16", "bf16") and kind != "lse":
         m = float(np.max(np.abs(ref))) if ref.size else 0.0
         return d / m if m > 0 else d

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert "gfx950" in fa.fa_version()
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert fa.fa_status_string(code).startswith("FA_")
     assert "unknown" in fa.fa_status_string(-99)
 
@@ -58,7 +58,7 @@ def _fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE + 4096, lse=FAKE + 8192, B=1, H=1, Sq=8,
     return lib.fa_fwd_tile(tile, *args)
 
 
-def _bwd(B=1, H=1, Sq=8, Sk=8, D=64, dtype=0, ptrs=None, strides=None, tiles=None):
+def _bwd(B=1, H=1, Sq=8, Sk=8, D=64, dtype=0, ptrs=None, strides=None, tiles=None, causal=0):
     p = dict(q=FAKE, k=FAKE + 1 * 4096, v=FAKE + 2 * 4096, o=FAKE + 3 * 4096,
              do=FAKE + 4 * 4096, lse=FAKE + 5 * 4096, delta=FAKE + 6 * 4096,
              dq=FAKE + 7 * 4096, dk=FAKE + 8 * 4096, dv=FAKE + 9 * 4096)
@@ -67,7 +67,7 @@ def _bwd(B=1, H=1, Sq=8, Sk=8, D=64, dtype=0, ptrs=None, strides=None, tiles=Non
     st.update(strides or {})
     vp = ctypes.c_void_p
     args = [vp(p["q"]), st["q"], vp(p["k"]), st["k"], vp(p["v"]), st["v"], vp(p["o"]), st["o"],
-            vp(p["do"]), st["do"], vp(p["lse"]), B, H, Sq, Sk, D, 0, ctypes.c_float(0.125),
+            vp(p["do"]), st["do"], vp(p["lse"]), B, H, Sq, Sk, D, causal, ctypes.c_float(0.125),
             dtype, vp(p["delta"]), vp(p["dq"]), st["dq"], vp(p["dk"]), st["dk"], vp(p["dv"]),
             st["dv"], vp(0)]
     if tiles is None:
@@ -77,6 +77,12 @@ def _bwd(B=1, H=1, Sq=8, Sk=8, D=64, dtype=0, ptrs=None, strides=None, tiles=Non
 
 def test_fwd_rejects_bad_dtype():
     assert _fwd(dtype=7) == -3
+
+
+def test_causal_mode_must_be_0_1_or_2():
+    assert _fwd(causal=3) == -8
+    assert _fwd(causal=-1) == -8
+    assert _bwd(causal=3) == -8
 
 
 @pytest.mark.parametrize("D", [0, 8, 48, 96, 256])

@@ -137,6 +137,32 @@ def test_rising_scores_rescale(dname, D, causal, t):
     check_full(case, x, got)
 
 
+BOTTOM_RIGHT = [
+    W.Case("br_sq_lt_sk_f16_D64", 1, 2, 100, 300, 64, "f16", 2, seed=500),
+    W.Case("br_sq_lt_sk_f16_D128", 1, 2, 200, 700, 128, "f16", 2, seed=501, layout="bshd"),
+    W.Case("br_sq_lt_sk_f32_D32", 2, 2, 37, 90, 32, "f32", 2, seed=502),
+    W.Case("br_sq_lt_sk_bf16_D128", 1, 2, 300, 1000, 128, "bf16", 2, seed=503),
+    W.Case("br_sq_gt_sk_f16_D64", 1, 2, 300, 100, 64, "f16", 2, seed=504),
+    W.Case("br_sq_gt_sk_f16_D128", 1, 2, 700, 200, 128, "f16", 2, seed=505, layout="bshd"),
+    W.Case("br_sq_gt_sk_f32_D16", 2, 2, 90, 37, 16, "f32", 2, seed=506),
+    W.Case("br_sq_gt_sk_bf16_D128", 1, 2, 1000, 333, 128, "bf16", 2, seed=507),
+    W.Case("br_sq_eq_sk_f16_D128", 1, 2, 333, 333, 128, "f16", 2, seed=508),
+    W.Case("br_one_key_f16_D128", 1, 2, 77, 1, 128, "f16", 2, seed=509),
+]
+
+
+@pytest.mark.parametrize("case", BOTTOM_RIGHT, ids=lambda c: c.name)
+def test_bottom_right_causal(case):
+    """causal = 2: query i sees keys j <= i + Sk - Sq; rows with no visible key
+    give O = 0, LSE = -inf and no gradient."""
+    x, got = run_case(case)
+    check_full(case, x, got)
+    if case.Sq > case.Sk:
+        n = case.Sq - case.Sk
+        assert np.all(got["o"][:, :, :n] == 0) and np.all(np.isneginf(got["lse"][:, :, :n]))
+        assert np.all(got["dq"][:, :, :n] == 0)
+
+
 @pytest.mark.parametrize("case", W.bf16_cases(), ids=lambda c: c.name)
 def test_bf16_cases(case):
     x, got = run_case(case)
@@ -198,6 +224,17 @@ def test_every_tile_configuration(dname, D, tiles, causal):
     Sq, Sk = (333, 333) if causal else (200, 333)
     case = W.Case(f"tiles_{dname}_D{D}_{tiles}_{causal}", 1, 2, Sq, Sk, D, dname, causal,
                   seed=200 + D)
+    x, got = run_case(case, tiles=tiles)
+    check_full(case, x, got)
+
+
+@pytest.mark.parametrize("dname,D,tiles", TILE_CASES,
+                         ids=[f"{d}-D{D}-t{t}" for d, D, t in TILE_CASES])
+@pytest.mark.parametrize("shape", [(200, 333), (333, 200)], ids=["sq<sk", "sq>sk"])
+def test_every_tile_configuration_bottom_right(dname, D, tiles, shape):
+    Sq, Sk = shape
+    case = W.Case(f"tiles_br_{dname}_D{D}_{tiles}_{Sq}x{Sk}", 1, 2, Sq, Sk, D, dname, 2,
+                  seed=600 + D)
     x, got = run_case(case, tiles=tiles)
     check_full(case, x, got)
 
