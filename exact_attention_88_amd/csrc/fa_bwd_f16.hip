@@ -322,16 +322,19 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   const int ntiles = a.Sq > qstart ? (a.Sq - qstart + BM - 1) / BM : 0;
   constexpr int PER = BM * 16 / NT;
   u32x4 qr[PER], dr[PER];
+  // LSE and delta of the staged rows are loaded raw, unconditionally (the row
+  // index clamped in bounds), and only converted when they are stored: a
+  // select on a loaded value at the load site would make the wave wait for
+  // that load, and with it for every tile load issued before it.
   float lsr = 0.f, dlr = 0.f;
+  bool lrow = false;
   auto load_rows = [&](int q0) {
     tile_load<BM, NT>(qr, qbase, a.q.ss, q0, a.Sq);
     tile_load<BM, NT>(dr, dobase, a.dout.ss, q0, a.Sq);
-    if ((int)threadIdx.x < BM) {
-      const int i = q0 + (int)threadIdx.x;
-      const float li = i < a.Sq ? lse[i] : INFINITY;  // LSE = -inf: no visible key, P = 0
-      lsr = li == -INFINITY ? INFINITY : li * kLog2e;
-      dlr = i < a.Sq ? dl[i] : 0.f;
-    }
+    const int i = q0 + ((int)threadIdx.x & (BM - 1));
+    lrow = i < a.Sq;
+    lsr = lse[min(i, a.Sq - 1)];
+    dlr = dl[min(i, a.Sq - 1)];
   };
   auto store_rows = [&](int buf) {
     T* base = smem + buf * BUF;
@@ -345,8 +348,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
       tile_store<BM, NT, kLST>(dr, base + 2 * TR + TT);
     }
     if ((int)threadIdx.x < BM) {
-      lsd[buf][0][threadIdx.x] = lsr;
-      lsd[buf][1][threadIdx.x] = dlr;
+      // Rows past the end, and rows with no visible key (LSE = -inf), get P = 0.
+      lsd[buf][0][threadIdx.x] = (!lrow || lsr == -INFINITY) ? INFINITY : lsr * kLog2e;
+      lsd[buf][1][threadIdx.x] = lrow ? dlr : 0.f;
     }
   };
   if (ntiles > 0) {
