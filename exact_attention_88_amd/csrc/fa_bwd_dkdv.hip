@@ -296,10 +296,10 @@ const TileCfg* dkdv_tile(int dtype, int D, int id) {
 
 int dkdv_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
   (void)Sq; (void)Sk; (void)causal;
-  // fp16, D = 128: the tuned kernel with 128-query tiles in the swizzled
-  // single-copy layout measured fastest on MI355X at S = 4096 and 16384,
-  // causal and not.
-  if (table_dt(dtype) == 0 && D == 128) return 3;
+  // 16-bit, D = 128: the software-pipelined tuned kernel (128-query tiles,
+  // swizzled single-copy layout, buffer loads into LDS) measured fastest on
+  // MI355X at every length from 512 to 16384, causal and not.
+  if (table_dt(dtype) == 0 && D == 128) return 4;
   return 0;
 }
 

@@ -447,6 +447,321 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   }
 }
 
+// ------------------------------------------- dK / dV, software-pipelined
+// The same work as dkdv_f16_d128 with 128-query tiles in the swizzled layout,
+// rearranged so that the LDS reads of one 32-query block overlap the MFMAs of
+// another:
+//   * Q and dO tiles go from global memory straight into LDS through buffer
+//     loads with an LDS destination.  Lane i of a wave writes its 16 bytes at
+//     the wave's LDS address + 16*i, so the swizzle is applied to the global
+//     chunk each lane fetches; rows at or past Sq fall outside the buffer's
+//     byte range and read as zero.  No staging registers are needed.
+//   * The row-wise Q and dO fragments of the next block (of the next tile,
+//     after the last block) are read while the dV and dK products of the
+//     current block run; the transposed fragments and the row statistics of a
+//     block are read while its S and dP products run.
+//   * One barrier per tile, inside its last block: after it the buffer just
+//     read is refilled with the tile after next, and the next tile's first
+//     fragments are read from the other buffer.
+//   * Only the tiles that straddle the causal diagonal carry masks.  Keys past
+//     Sk are not masked: their dK and dV columns depend on nothing else and
+//     are never stored.
+// Needs 32-bit byte offsets: (Sq + 3*128) * row stride * 2 bytes < 2^31 for
+// Q and dO, and a row stride of at least 128 elements (checked on the host).
+template <bool V> struct BoolTag { static constexpr bool value = V; };
+typedef int rsrc_t __attribute__((ext_vector_type(4)));  // buffer resource (4 SGPRs)
+
+// Raw buffer over [base, base + nbytes): stride 0, 32-bit data format.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int nbytes) {
+  const uint64_t p = (uint64_t)base;
+  rsrc_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(p & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One wave-wide 16-byte-per-lane buffer load into LDS at lds (wave-uniform):
+// lane i's bytes land at lds + 16*i.  Issued as inline assembly so that the
+// compiler does not make every later LDS read wait for it: the caller waits
+// (vmcnt(0)) before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(rsrc_t r, const void* lds, int voff) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(__attribute__((address_space(3))) const void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
+
+// 128 rows x 256 bytes into the swizzled layout at lds: 32 wave-wide 1 KB
+// loads (4 rows each) shared by the NW waves.
+template <int NW, class T>
+__device__ __forceinline__ void tile_dma128(rsrc_t r, T* lds, int64_t ss, int row0) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int r0 = (i * NW + w) * 4;
+    const int row = r0 + (lane >> 4);
+    const int chunk = (lane & 15) ^ swz(row);
+    const int off = (int)((int64_t)(row0 + row) * ss * (int64_t)sizeof(T)) + chunk * 16;
+    dma16(r, lds + r0 * kD, off);
+  }
+}
+
+template <class T, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
+  constexpr int BM = 128, NW = 4, BN = 32 * NW, NQB = BM / 32, TR = BM * kD, BUF = 2 * TR;
+  __shared__ __attribute__((aligned(1024))) T smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) float lsd[2][2][BM];  // [buffer][LSE*log2e, delta][row]
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
+  const int nkb = (a.Sk + BN - 1) / BN;
+  const int L = xcd_logical_block();
+  const int kb = L % nkb;
+  const int bh = L / nkb;
+  const int b = bh / a.H, h = bh % a.H;
+  const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
+  const T* dobase = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh;
+  const rsrc_t rq = make_rsrc(qbase, (int)((int64_t)a.Sq * a.q.ss * (int64_t)sizeof(T)));
+  const rsrc_t rd = make_rsrc(dobase, (int)((int64_t)a.Sq * a.dout.ss * (int64_t)sizeof(T)));
+  const float* lse = a.lse + (int64_t)bh * a.Sq;
+  const float* dl = a.delta + (int64_t)bh * a.Sq;
+  const int k0 = kb * BN, kw = k0 + w * 32, kj = kw + c;
+
+  V8<T> kf[8], vf[8];
+  {
+    const int kc = min(kj, a.Sk - 1);
+    const T* krow = (const T*)a.k.p + b * a.k.sb + h * a.k.sh + (int64_t)kc * a.k.ss;
+    const T* vrow = (const T*)a.v.p + b * a.v.sb + h * a.v.sh + (int64_t)kc * a.v.ss;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      kf[ks] = *reinterpret_cast<const V8<T>*>(krow + ks * 16 + g * 8);
+      vf[ks] = *reinterpret_cast<const V8<T>*>(vrow + ks * 16 + g * 8);
+    }
+  }
+  // K and V resident before any buffer load into LDS is issued: the compiler
+  // does not count those loads, so a wait it places for K or V later would
+  // also wait for them.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { dk[i] = zero16(); dv[i] = zero16(); }
+  const float cs = a.scale_log2;
+
+  const int qstart = CAUSAL ? (max(0, k0 - a.coff) / BM) * BM : 0;
+  const int ntiles = a.Sq > qstart ? (a.Sq - qstart + BM - 1) / BM : 0;
+  // Tile t is wholly visible when its first query sees the block's last key:
+  // qstart + t*BM + coff >= k0 + BN - 1.  The tiles before that carry masks.
+  const int hidden = k0 + BN - 1 - a.coff - qstart;
+  const int nmask = CAUSAL ? min(ntiles, hidden > 0 ? (hidden + BM - 1) / BM : 0) : 0;
+
+  // LSE and delta of row (tile start + thread % 128), loaded raw and converted
+  // when stored (see dkdv_f16_d128).
+  float lsr = 0.f, dlr = 0.f;
+  bool lrow = false;
+  auto issue_tile = [&](int t, T* base) {
+    const int q0 = qstart + t * BM;
+    tile_dma128<NW>(rq, base, a.q.ss, q0);
+    tile_dma128<NW>(rd, base + TR, a.dout.ss, q0);
+    const int i = q0 + ((int)threadIdx.x & (BM - 1));
+    lrow = i < a.Sq;
+    lsr = lse[min(i, a.Sq - 1)];
+    dlr = dl[min(i, a.Sq - 1)];
+  };
+  auto store_rows = [&](int t) {
+    if ((int)threadIdx.x < BM) {
+      lsd[t & 1][0][threadIdx.x] = (!lrow || lsr == -INFINITY) ? INFINITY : lsr * kLog2e;
+      lsd[t & 1][1][threadIdx.x] = lrow ? dlr : 0.f;
+    }
+  };
+
+  // Pipeline state carried from 32-query block j-1 into block j.
+  V8<T> qf[8];         // Q rows of block j (operand of S)
+  V8<T> qtp[2][4];     // transposed Q of block j-1 (operand of dK)
+  f32x16 pc, dpc;      // P and dP of block j-1
+  float4 dc[4];        // delta of block j-1
+  V8<T> sf0;           // dS of block j-1, rows of k-step 0, rounded
+  pc = zero16();
+  dpc = zero16();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sf0[e] = (T)0.f;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) qtp[tt][db] = sf0;
+  if (ntiles > 0) {
+    issue_tile(0, smem);
+    store_rows(0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS
+    __syncthreads();
+    if (ntiles > 1) issue_tile(1, smem + BUF);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(smem, 0, ks * 2);
+  }
+
+  // Rows of k-step tt of an accumulator (crow order) out of four float4 runs.
+  auto sel = [](const float4* v, int r) {
+    return r % 4 == 0 ? v[r / 4].x : r % 4 == 1 ? v[r / 4].y : r % 4 == 2 ? v[r / 4].z : v[r / 4].w;
+  };
+
+  // Tile t: its data is in cur, the next tile's in nxt.  Block j runs four
+  // phases, each one scheduling region whose eight MFMAs are interleaved with
+  // the LDS reads and the VALU work listed for it (a wave issues only a few
+  // VALU instructions per MFMA without stalling the matrix pipe, so the
+  // softmax-gradient arithmetic is spread evenly over all four):
+  //   1: S(j) = Q K^T        | read dO rows(j), LSE(j), delta(j) | dS(j-1), second half
+  //   2: dK += dS(j-1)^T Q   | read dO^T(j), Q^T(j)             | P(j), first half
+  //   3: dP(j) = dO V^T      | read Q rows(j+1)                 | P(j), second half
+  //   4: dV += P(j)^T dO     |                                  | dS(j), first half
+  // Phase 2 holds the block's last reads of cur, so the tile's barrier sits
+  // between phases 2 and 3 of its last block; phase 3 of that block reads the
+  // next tile's first rows from nxt.
+  auto tile = [&](auto masked, int t, T* cur, T* nxt) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const int q0 = qstart + t * BM;
+    const T* Qc = cur;
+    const T* Dc = Qc + TR;
+    const T* Qn = nxt;
+    const float* Ls = lsd[t & 1][0];
+    const float* Dl = lsd[t & 1][1];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qs = q0 + qb * 32;
+      V8<T> of[8], dt[2][4], qt[2][4], sf1, pf0, pf1;
+      float4 l4[4], d4[4];
+      f32x16 s = zero16(), dp = zero16(), p;
+      // ---- 1
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r_swz(Dc, qb * 32, ks * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        l4[i] = *reinterpret_cast<const float4*>(Ls + qb * 32 + i * 8 + g * 4);
+        d4[i] = *reinterpret_cast<const float4*>(Dl + qb * 32 + i * 8 + g * 4);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) s = Mfma<T>::mma(qf[ks], kf[ks], s);
+      {
+        f32x16 x;
+#pragma unroll
+        for (int r = 8; r < 16; ++r) x[r] = pc[r] * (dpc[r] - sel(dc, r));
+        sf1 = cvt8<T>(x, 1);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- 2
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dt[tt][db] = frag_t_swz(Dc, qb * 32, tt, db * 32);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) qt[tt][db] = frag_t_swz(Qc, qb * 32, tt, db * 32);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) dk[db] = Mfma<T>::mma(qtp[0][db], sf0, dk[db]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) dk[db] = Mfma<T>::mma(qtp[1][db], sf1, dk[db]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        p[r] = fast_exp2(__builtin_fmaf(s[r], cs, -sel(l4, r)));
+        if (MASKED && kj > qs + a.coff + crow(r, g)) p[r] = 0.f;
+      }
+      pf0 = cvt8<T>(p, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (qb == NQB - 1) {
+        // Every wave is done reading this buffer: refill it with the tile
+        // after next, and publish the next tile's data and row statistics.
+        store_rows(t + 1);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's buffer loads are in LDS
+        __syncthreads();
+        if (t + 2 < ntiles) issue_tile(t + 2, cur);
+      }
+      // ---- 3
+      {
+        const T* nq = qb + 1 < NQB ? Qc : Qn;
+        const int nr = ((qb + 1) % NQB) * 32;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(nq, nr, ks * 2);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) dp = Mfma<T>::mma(of[ks], vf[ks], dp);
+#pragma unroll
+      for (int r = 8; r < 16; ++r) {
+        p[r] = fast_exp2(__builtin_fmaf(s[r], cs, -sel(l4, r)));
+        if (MASKED && kj > qs + a.coff + crow(r, g)) p[r] = 0.f;
+      }
+      pf1 = cvt8<T>(p, 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- 4
+#pragma unroll
+      for (int db = 0; db < 4; ++db) dv[db] = Mfma<T>::mma(dt[0][db], pf0, dv[db]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) dv[db] = Mfma<T>::mma(dt[1][db], pf1, dv[db]);
+      {
+        f32x16 x;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) x[r] = p[r] * (dp[r] - sel(d4, r));
+        sf0 = cvt8<T>(x, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      pc = p;
+      dpc = dp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dc[i] = d4[i];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) qtp[tt][db] = qt[tt][db];
+    }
+  };
+  int t = 0;
+  for (; t < nmask; ++t) tile(BoolTag<true>{}, t, smem + (t & 1) * BUF, smem + ((t + 1) & 1) * BUF);
+  for (; t < ntiles; ++t) tile(BoolTag<false>{}, t, smem + (t & 1) * BUF, smem + ((t + 1) & 1) * BUF);
+  // Drain: the second half of the last block's dS, and its dK product.
+  if (ntiles > 0) {
+    f32x16 x;
+#pragma unroll
+    for (int r = 8; r < 16; ++r) x[r] = pc[r] * (dpc[r] - sel(dc, r));
+    const V8<T> sf1 = cvt8<T>(x, 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) dk[db] = Mfma<T>::mma(qtp[0][db], sf0, dk[db]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) dk[db] = Mfma<T>::mma(qtp[1][db], sf1, dk[db]);
+  }
+
+  if (kj < a.Sk) {
+    T* dkrow = (T*)a.dk.p + b * a.dk.sb + h * a.dk.sh + (int64_t)kj * a.dk.ss;
+    T* dvrow = (T*)a.dv.p + b * a.dv.sb + h * a.dv.sh + (int64_t)kj * a.dv.ss;
+    store_row4x4(dkrow, dk, a.scale, g);
+    store_row4x4(dvrow, dv, 1.f, g);
+  }
+}
+
 template <class T, int BN, int NW, bool CAUSAL, bool SWZ>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
   constexpr int BM = 32 * NW;
@@ -465,6 +780,23 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
   return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_f16_d128<T, BM, NW, CAUSAL, SWZ>),
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
+}
+
+// Byte offsets of every Q and dO row the pipelined dK/dV kernel may address
+// (up to 3 tiles past Sq) fit in 31 bits, and rows do not overlap.
+bool dkdv_pipe_fits(const BwdArgs& a, int esize) {
+  const int64_t lim = (int64_t)1 << 31;
+  return a.q.ss >= kD && a.dout.ss >= kD && ((int64_t)a.Sq + 3 * 128) * a.q.ss * esize < lim &&
+         ((int64_t)a.Sq + 3 * 128) * a.dout.ss * esize < lim;
+}
+
+template <class T, bool CAUSAL>
+hipError_t launch_dkdv_pipe(const BwdArgs& a, hipStream_t s) {
+  const int64_t grid = (((int64_t)a.Sk + 127) / 128) * a.B * a.H;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_pipe_d128<T, CAUSAL>),
+                         dim3((unsigned)grid), dim3(256), args, 0, s);
 }
 
 }  // namespace
@@ -495,12 +827,14 @@ hipError_t launch_dq_fast(const BwdArgs& a, int v, int dtype, int causal, hipStr
 }
 
 // dK/dV variants: 0 = (BM 64, 4 waves), 1 = (BM 32, 4 waves), 2 = (BM 64,
-// 4 waves, swizzled single-copy Q and dO), 3 = (BM 128, 4 waves, swizzled).  (With 8 waves, two per SIMD, the
+// 4 waves, swizzled single-copy Q and dO), 3 = (BM 128, 4 waves, swizzled),
+// 4 = variant 3 software-pipelined with buffer loads into LDS (variant 3 runs
+// instead where its 31-bit offsets do not reach every row).  (With 8 waves, two per SIMD, the
 // 32 keys' K, V, dK and dV no longer fit the 256 registers a wave then gets,
 // and the compiler spills.)
-int dkdv_fast_variants() { return 4; }
+int dkdv_fast_variants() { return 5; }
 TileCfg dkdv_fast_cfg(int v) {
-  const int bm = v == 1 ? 32 : v == 3 ? 128 : 64, nw = 4;
+  const int bm = v == 1 ? 32 : v >= 3 ? 128 : 64, nw = 4;
   const int row_halfs = v >= 2 ? 2 * kD : 2 * kLSR + 2 * kLST;
   return TileCfg{bm, 32 * nw, nw, 2 * bm * row_halfs * 2 + 2 * 2 * bm * 4};
 }
@@ -511,6 +845,9 @@ hipError_t launch_dkdv_variant(const BwdArgs& a, int v, int causal, hipStream_t 
     case 1: return causal ? launch_dkdv_t<T, 32, 4, true, false>(a, s) : launch_dkdv_t<T, 32, 4, false, false>(a, s);
     case 2: return causal ? launch_dkdv_t<T, 64, 4, true, true>(a, s) : launch_dkdv_t<T, 64, 4, false, true>(a, s);
     case 3: return causal ? launch_dkdv_t<T, 128, 4, true, true>(a, s) : launch_dkdv_t<T, 128, 4, false, true>(a, s);
+    case 4:
+      if (!dkdv_pipe_fits(a, (int)sizeof(T))) return launch_dkdv_variant<T>(a, 3, causal, s);
+      return causal ? launch_dkdv_pipe<T, true>(a, s) : launch_dkdv_pipe<T, false>(a, s);
   }
   return hipErrorInvalidValue;
 }
