@@ -512,7 +512,7 @@ template <class T, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   constexpr int BM = 128, NW = 4, BN = 32 * NW, NQB = BM / 32, TR = BM * kD, BUF = 2 * TR;
   __shared__ __attribute__((aligned(1024))) T smem[2 * BUF];
-  __shared__ __attribute__((aligned(16))) float lsd[2][2][BM];  // [buffer][LSE*log2e, delta][row]
+  __shared__ __attribute__((aligned(16))) float lsd[2][2][BM];  // [buffer][LSE*log2e, -delta][row]
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nkb = (a.Sk + BN - 1) / BN;
@@ -572,20 +572,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   auto store_rows = [&](int t) {
     if ((int)threadIdx.x < BM) {
       lsd[t & 1][0][threadIdx.x] = (!lrow || lsr == -INFINITY) ? INFINITY : lsr * kLog2e;
-      lsd[t & 1][1][threadIdx.x] = lrow ? dlr : 0.f;
+      lsd[t & 1][1][threadIdx.x] = lrow ? -dlr : 0.f;
     }
   };
 
   // Pipeline state carried from 32-query block j-1 into block j.
   V8<T> qf[8];         // Q rows of block j (operand of S)
   V8<T> qtp[2][4];     // transposed Q of block j-1 (operand of dK)
-  f32x16 pc, dpc;      // P and dP of block j-1
-  float4 dc[4];        // delta of block j-1
+  f32x16 pc, dpc;      // P and dP - delta of block j-1
   V8<T> sf0;           // dS of block j-1, rows of k-step 0, rounded
   pc = zero16();
   dpc = zero16();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int e = 0; e < 8; ++e) sf0[e] = (T)0.f;
 #pragma unroll
@@ -631,22 +628,23 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
     for (int qb = 0; qb < NQB; ++qb) {
       const int qs = q0 + qb * 32;
       V8<T> of[8], dt[2][4], qt[2][4], sf1, pf0, pf1;
-      float4 l4[4], d4[4];
-      f32x16 s = zero16(), dp = zero16(), p;
+      float4 l4[4];
+      f32x16 s = zero16(), dp, p;  // dp starts from -delta: dP - delta comes out of the MFMAs
       // ---- 1
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r_swz(Dc, qb * 32, ks * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         l4[i] = *reinterpret_cast<const float4*>(Ls + qb * 32 + i * 8 + g * 4);
-        d4[i] = *reinterpret_cast<const float4*>(Dl + qb * 32 + i * 8 + g * 4);
+        const float4 d = *reinterpret_cast<const float4*>(Dl + qb * 32 + i * 8 + g * 4);
+        dp[i * 4 + 0] = d.x; dp[i * 4 + 1] = d.y; dp[i * 4 + 2] = d.z; dp[i * 4 + 3] = d.w;
       }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) s = Mfma<T>::mma(qf[ks], kf[ks], s);
       {
         f32x16 x;
 #pragma unroll
-        for (int r = 8; r < 16; ++r) x[r] = pc[r] * (dpc[r] - sel(dc, r));
+        for (int r = 8; r < 16; ++r) x[r] = pc[r] * dpc[r];
         sf1 = cvt8<T>(x, 1);
       }
 #pragma unroll
@@ -720,7 +718,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
       {
         f32x16 x;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) x[r] = p[r] * (dp[r] - sel(d4, r));
+        for (int r = 0; r < 8; ++r) x[r] = p[r] * dp[r];
         sf0 = cvt8<T>(x, 0);
       }
 #pragma unroll
@@ -731,8 +729,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       pc = p;
       dpc = dp;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dc[i] = d4[i];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -746,7 +742,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   if (ntiles > 0) {
     f32x16 x;
 #pragma unroll
-    for (int r = 8; r < 16; ++r) x[r] = pc[r] * (dpc[r] - sel(dc, r));
+    for (int r = 8; r < 16; ++r) x[r] = pc[r] * dpc[r];
     const V8<T> sf1 = cvt8<T>(x, 1);
 #pragma unroll
     for (int db = 0; db < 4; ++db) dk[db] = Mfma<T>::mma(qtp[0][db], sf0, dk[db]);
