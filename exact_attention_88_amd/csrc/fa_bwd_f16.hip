@@ -578,6 +578,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
 
   // Pipeline state carried from 32-query block j-1 into block j.
   V8<T> qf[8];         // Q rows of block j (operand of S)
+  V8<T> of[8];         // dO rows of block j (operand of dP)
   V8<T> qtp[2][4];     // transposed Q of block j-1 (operand of dK)
   f32x16 pc, dpc;      // P and dP - delta of block j-1
   V8<T> sf0;           // dS of block j-1, rows of k-step 0, rounded
@@ -597,6 +598,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
     if (ntiles > 1) issue_tile(1, smem + BUF);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(smem, 0, ks * 2);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r_swz(smem + TR, 0, ks * 2);
   }
 
   // Rows of k-step tt of an accumulator (crow order) out of four float4 runs.
@@ -609,13 +612,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   // the LDS reads and the VALU work listed for it (a wave issues only a few
   // VALU instructions per MFMA without stalling the matrix pipe, so the
   // softmax-gradient arithmetic is spread evenly over all four):
-  //   1: S(j) = Q K^T        | read dO rows(j), LSE(j), delta(j) | dS(j-1), second half
-  //   2: dK += dS(j-1)^T Q   | read dO^T(j), Q^T(j)             | P(j), first half
-  //   3: dP(j) = dO V^T      | read Q rows(j+1)                 | P(j), second half
-  //   4: dV += P(j)^T dO     |                                  | dS(j), first half
+  //   1: S(j) = Q K^T        | read dO^T(j), LSE(j), delta(j) | dS(j-1), second half
+  //   2: dK += dS(j-1)^T Q   | read Q^T(j)                    | P(j), first half
+  //   3: dP(j) = dO V^T      | read Q rows(j+1)               | P(j), second half
+  //   4: dV += P(j)^T dO     | read dO rows(j+1)              | dS(j), first half
   // Phase 2 holds the block's last reads of cur, so the tile's barrier sits
   // between phases 2 and 3 of its last block; phase 3 of that block reads the
-  // next tile's first rows from nxt.
+  // next tile's first rows from nxt, and so does phase 4.
   auto tile = [&](auto masked, int t, T* cur, T* nxt) {
     constexpr bool MASKED = decltype(masked)::value;
     const int q0 = qstart + t * BM;
@@ -627,12 +630,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qs = q0 + qb * 32;
-      V8<T> of[8], dt[2][4], qt[2][4], sf1, pf0, pf1;
+      V8<T> dt[2][4], qt[2][4], sf1, pf0, pf1;
       float4 l4[4];
       f32x16 s = zero16(), dp, p;  // dp starts from -delta: dP - delta comes out of the MFMAs
       // ---- 1
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r_swz(Dc, qb * 32, ks * 2);
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dt[tt][db] = frag_t_swz(Dc, qb * 32, tt, db * 32);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         l4[i] = *reinterpret_cast<const float4*>(Ls + qb * 32 + i * 8 + g * 4);
@@ -650,15 +655,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- 2
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dt[tt][db] = frag_t_swz(Dc, qb * 32, tt, db * 32);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -676,7 +677,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -689,12 +690,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
         if (t + 2 < ntiles) issue_tile(t + 2, cur);
       }
       // ---- 3
-      {
-        const T* nq = qb + 1 < NQB ? Qc : Qn;
-        const int nr = ((qb + 1) % NQB) * 32;
+      const T* nq = qb + 1 < NQB ? Qc : Qn;
+      const int nr = ((qb + 1) % NQB) * 32;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(nq, nr, ks * 2);
-      }
+      for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(nq, nr, ks * 2);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) dp = Mfma<T>::mma(of[ks], vf[ks], dp);
 #pragma unroll
@@ -712,6 +711,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       // ---- 4
 #pragma unroll
+      for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r_swz(nq + TR, nr, ks * 2);
+#pragma unroll
       for (int db = 0; db < 4; ++db) dv[db] = Mfma<T>::mma(dt[0][db], pf0, dv[db]);
 #pragma unroll
       for (int db = 0; db < 4; ++db) dv[db] = Mfma<T>::mma(dt[1][db], pf1, dv[db]);
@@ -724,6 +725,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
