@@ -223,10 +223,10 @@ const TileCfg* dq_tile(int dtype, int D, int id) {
 
 int dq_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
   (void)Sq; (void)Sk; (void)causal;
-  // fp16, D = 128: the tuned kernel with 8 waves and 64-key tiles in the
-  // swizzled single-copy layout measured fastest on MI355X at S = 4096 and
-  // 16384, causal and not.
-  if (table_dt(dtype) == 0 && D == 128) return 4;
+  // 16-bit, D = 128: the tuned kernel with 8 waves, 64-key tiles in the
+  // swizzled single-copy layout and buffer loads into LDS measured fastest on
+  // MI355X at S = 4096 and 16384, causal and not.
+  if (table_dt(dtype) == 0 && D == 128) return 5;
   return 0;
 }
 

@@ -23,12 +23,14 @@
 // live in registers, Q and dO stream in both layouts with LSE and delta.
 #include "fa_args.h"
 #include "fa_common.h"
+#include "fa_lds.h"
 
 namespace fa {
 
 namespace {
 
-constexpr int kD = 128;
+using namespace swzl;
+
 constexpr int kLSR = kD + 8;   // row-read layout stride (halfs): 272 bytes
 constexpr int kLST = kD + 32;  // transposed-read layout stride (halfs): 320 bytes
 
@@ -83,51 +85,6 @@ __device__ __forceinline__ V8<T> frag_t(const T* lds, int rbase, int t, int cbas
   r[0] = ah[0]; r[1] = ah[1]; r[2] = ah[2]; r[3] = ah[3];
   r[4] = bh[0]; r[5] = bh[1]; r[6] = bh[2]; r[7] = bh[3];
   return r;
-}
-
-// Single-copy swizzled layout: unpadded 256-byte rows in which the 16-byte
-// chunk k of row r sits at chunk position k ^ swz(r).  swz(r) takes distinct
-// values on any 16 consecutive rows (so 16-row ds_read_b128 row reads and
-// full-row stores are conflict free) and, on 4 rows that start at a multiple
-// of 4, spreads 4 neighbouring chunks over all 16 chunk positions (so 4-row
-// transposed reads are conflict free).  One layout serves both read patterns.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-template <int ROWS, int NT, class T>
-__device__ __forceinline__ void tile_store_swz(const u32x4* r, T* lds) {
-  constexpr int PER = ROWS * 16 / NT;
-  static_assert(NT % 256 == 0, "every thread keeps its row residue mod 16");
-  const int row0 = (int)threadIdx.x >> 4, off = row0 * kD + (((threadIdx.x & 15) ^ swz(row0)) << 3);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) *reinterpret_cast<u32x4*>(lds + i * (NT / 16) * kD + off) = r[i];
-}
-
-// Row-wise fragment in the swizzled layout; rbase is a multiple of 16.
-template <class T>
-__device__ __forceinline__ V8<T> frag_r_swz(const T* lds, int rbase, int kchunk) {
-  const int lane = threadIdx.x & 63, r = lane & 31;
-  return *reinterpret_cast<const V8<T>*>(lds + (rbase + r) * kD +
-                                      (((kchunk + (lane >> 5)) ^ swz(r)) << 3));
-}
-
-// Transposed fragment in the swizzled layout (same lanes as frag_t); rbase is
-// a multiple of 16 and cbase of 8.
-template <class T>
-__device__ __forceinline__ V8<T> frag_t_swz(const T* lds, int rbase, int t, int cbase) {
-  const int lane = threadIdx.x & 63, g = lane >> 5, j = lane & 15;
-  const int col = ((lane >> 4) & 1) * 16 + (j & 3) * 4;
-  const int r = g * 4 + (j >> 2);
-  const int ch = (cbase >> 3) + (col >> 3);
-  typedef __attribute__((address_space(3))) s4 lds_s4;
-  const T* p0 = lds + (rbase + t * 16 + r) * kD + ((ch ^ swz(r)) << 3) + (col & 7);
-  const T* p1 = lds + (rbase + t * 16 + r + 8) * kD + ((ch ^ swz(r + 8)) << 3) + (col & 7);
-  s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
-  s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1));
-  V4<T> ah = __builtin_bit_cast(V4<T>, a), bh = __builtin_bit_cast(V4<T>, b);
-  V8<T> x;
-  x[0] = ah[0]; x[1] = ah[1]; x[2] = ah[2]; x[3] = ah[3];
-  x[4] = bh[0]; x[5] = bh[1]; x[6] = bh[2]; x[7] = bh[3];
-  return x;
 }
 
 // Accumulator registers t*8 .. t*8+7 rounded to T (round to nearest even).
@@ -468,46 +425,6 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
 //     are never stored.
 // Needs 32-bit byte offsets: (Sq + 3*128) * row stride * 2 bytes < 2^31 for
 // Q and dO, and a row stride of at least 128 elements (checked on the host).
-template <bool V> struct BoolTag { static constexpr bool value = V; };
-typedef int rsrc_t __attribute__((ext_vector_type(4)));  // buffer resource (4 SGPRs)
-
-// Raw buffer over [base, base + nbytes): stride 0, 32-bit data format.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int nbytes) {
-  const uint64_t p = (uint64_t)base;
-  rsrc_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(p & 0xffffffffu));
-  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// One wave-wide 16-byte-per-lane buffer load into LDS at lds (wave-uniform):
-// lane i's bytes land at lds + 16*i.  Issued as inline assembly so that the
-// compiler does not make every later LDS read wait for it: the caller waits
-// (vmcnt(0)) before the barrier that publishes the data.
-__device__ __forceinline__ void dma16(rsrc_t r, const void* lds, int voff) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)(__attribute__((address_space(3))) const void*)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
-}
-
-// 128 rows x 256 bytes into the swizzled layout at lds: 32 wave-wide 1 KB
-// loads (4 rows each) shared by the NW waves.
-template <int NW, class T>
-__device__ __forceinline__ void tile_dma128(rsrc_t r, T* lds, int64_t ss, int row0) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < 32 / NW; ++i) {
-    const int r0 = (i * NW + w) * 4;
-    const int row = r0 + (lane >> 4);
-    const int chunk = (lane & 15) ^ swz(row);
-    const int off = (int)((int64_t)(row0 + row) * ss * (int64_t)sizeof(T)) + chunk * 16;
-    dma16(r, lds + r0 * kD, off);
-  }
-}
-
 template <class T, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   constexpr int BM = 128, NW = 4, BN = 32 * NW, NQB = BM / 32, TR = BM * kD, BUF = 2 * TR;
@@ -562,8 +479,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   bool lrow = false;
   auto issue_tile = [&](int t, T* base) {
     const int q0 = qstart + t * BM;
-    tile_dma128<NW>(rq, base, a.q.ss, q0);
-    tile_dma128<NW>(rd, base + TR, a.dout.ss, q0);
+    tile_dma<BM, NW>(rq, base, a.q.ss, q0);
+    tile_dma<BM, NW>(rd, base + TR, a.dout.ss, q0);
     const int i = q0 + ((int)threadIdx.x & (BM - 1));
     lrow = i < a.Sq;
     lsr = lse[min(i, a.Sq - 1)];
@@ -780,8 +697,142 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
 }
 
+// ------------------------------------------------ dQ, buffer loads into LDS
+// dq_f16_d128 with 64-key tiles in the swizzled layout and 8 waves, with the
+// K and V tiles loaded straight into LDS by buffer loads (no staging
+// registers; keys at or past Sk read as zero and are masked) and the dP^T
+// accumulators starting from -delta, so that dS = P * (dP - delta) is one
+// multiply per element.  The registers the staging held pay for the -delta
+// start.  Needs the 31-bit offsets the dK/dV kernel needs, for K and V.
+template <class T, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
+  constexpr int NW = 8, BM = 32 * NW, BN = 64, NT = NW * 64, NKB = BN / 32;
+  constexpr int TR = BN * kD, BUF = 2 * TR;  // K rows, V rows
+  __shared__ __attribute__((aligned(1024))) T smem[2 * BUF];
+  (void)NT;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
+  const int nqb = (a.Sq + BM - 1) / BM;
+  const int L = xcd_logical_block();
+  int qb = L % nqb;
+  const int bh = L / nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+  const int b = bh / a.H, h = bh % a.H;
+  const T* kbase = (const T*)a.k.p + b * a.k.sb + h * a.k.sh;
+  const T* vbase = (const T*)a.v.p + b * a.v.sb + h * a.v.sh;
+  const rsrc_t rk = make_rsrc(kbase, (int)((int64_t)a.Sk * a.k.ss * (int64_t)sizeof(T)));
+  const rsrc_t rv = make_rsrc(vbase, (int)((int64_t)a.Sk * a.v.ss * (int64_t)sizeof(T)));
+  const int q0 = qb * BM, qw = q0 + w * 32, qi = qw + c;
+  const bool valid = qi < a.Sq;
+
+  V8<T> qf[8], df[8];
+  {
+    const int qc = min(qi, a.Sq - 1);
+    const T* qrow = (const T*)a.q.p + b * a.q.sb + h * a.q.sh + (int64_t)qc * a.q.ss;
+    const T* drow =
+        (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh + (int64_t)qc * a.dout.ss;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[ks] = *reinterpret_cast<const V8<T>*>(qrow + ks * 16 + g * 8);
+      df[ks] = *reinterpret_cast<const V8<T>*>(drow + ks * 16 + g * 8);
+    }
+  }
+  // Rows past the end, and rows with no visible key (LSE = -inf), get P = 0.
+  const float lse_n = valid ? a.lse[(int64_t)bh * a.Sq + qi] : INFINITY;
+  const float lse2 = lse_n == -INFINITY ? INFINITY : lse_n * kLog2e;
+  const float dlt = valid ? a.delta[(int64_t)bh * a.Sq + qi] : 0.f;
+  // Row data resident before any buffer load into LDS is issued (the compiler
+  // does not count those).
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  f32x16 ndl;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl[r] = -dlt;
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dq[i] = zero16();
+  const float cs = a.scale_log2;
+
+  const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
+  const int ntiles = (kend + BN - 1) / BN;
+  auto issue_tile = [&](int t) {
+    T* base = smem + (t & 1) * BUF;
+    tile_dma<BN, NW>(rk, base, a.k.ss, t * BN);
+    tile_dma<BN, NW>(rv, base + TR, a.v.ss, t * BN);
+  };
+  if (ntiles > 0) issue_tile(0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    const T* Kr = smem + (t & 1) * BUF;
+    const T* Vr = Kr + TR;
+    // The other buffer was last read in tile t-1, before the barrier below.
+    if (t + 1 < ntiles) issue_tile(t + 1);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int ks0 = k0 + kb * 32;
+      if (CAUSAL && ks0 > qw + a.coff + 31) continue;
+      V8<T> kf[8], vf[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kf[ks] = frag_r_swz(Kr, kb * 32, ks * 2);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) vf[ks] = frag_r_swz(Vr, kb * 32, ks * 2);
+      f32x16 s = zero16(), dp = ndl;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) s = Mfma<T>::mma(kf[ks], qf[ks], s);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) dp = Mfma<T>::mma(vf[ks], df[ks], dp);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = fast_exp2(__builtin_fmaf(s[r], cs, -lse2));
+      // Masks only on the diagonal block and the ragged key tail.
+      if ((ks0 + 32 > a.Sk) || (CAUSAL && ks0 + 31 > qw + a.coff)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = ks0 + crow(r, g);
+          if (key >= a.Sk || (CAUSAL && key > qi + a.coff)) s[r] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = s[r] * dp[r];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        V8<T> kt[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) kt[db] = frag_t_swz(Kr, kb * 32, tt, db * 32);
+        const V8<T> sf = cvt8<T>(s, tt);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dq[db] = Mfma<T>::mma(kt[db], sf, dq[db]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's buffer loads are in LDS
+    __syncthreads();
+  }
+
+  if (valid) {
+    T* row = (T*)a.dq.p + b * a.dq.sb + h * a.dq.sh + (int64_t)qi * a.dq.ss;
+    store_row4x4(row, dq, a.scale, g);
+  }
+}
+
 // Byte offsets of every Q and dO row the pipelined dK/dV kernel may address
 // (up to 3 tiles past Sq) fit in 31 bits, and rows do not overlap.
+bool dq_pipe_fits(const BwdArgs& a, int esize) {
+  const int64_t lim = (int64_t)1 << 31;
+  return a.k.ss >= kD && a.v.ss >= kD && ((int64_t)a.Sk + 3 * 64) * a.k.ss * esize < lim &&
+         ((int64_t)a.Sk + 3 * 64) * a.v.ss * esize < lim;
+}
+
+template <class T, bool CAUSAL>
+hipError_t launch_dq_pipe(const BwdArgs& a, hipStream_t s) {
+  const int64_t grid = (((int64_t)a.Sq + 255) / 256) * a.B * a.H;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_pipe_d128<T, CAUSAL>),
+                         dim3((unsigned)grid), dim3(512), args, 0, s);
+}
+
 bool dkdv_pipe_fits(const BwdArgs& a, int esize) {
   const int64_t lim = (int64_t)1 << 31;
   return a.q.ss >= kD && a.dout.ss >= kD && ((int64_t)a.Sq + 3 * 128) * a.q.ss * esize < lim &&
@@ -800,9 +851,11 @@ hipError_t launch_dkdv_pipe(const BwdArgs& a, hipStream_t s) {
 }  // namespace
 
 // dQ variants: 0 = (BN 64, 8 waves), 1 = (BN 64, 4 waves), 2 = (BN 32, 8 waves);
-// 3, 4 = (BN 32, 64; 8 waves) with swizzled single-copy K and V.  (With
-// 128-key tiles the staging registers push the non-causal kernel into spills.)
-int dq_fast_variants() { return 5; }
+// 3, 4 = (BN 32, 64; 8 waves) with swizzled single-copy K and V; 5 = variant
+// 4 with buffer loads into LDS and dP starting from -delta (variant 4 runs
+// instead where its 31-bit offsets do not reach every row).  (With 128-key
+// tiles the staging registers push the non-causal kernel into spills.)
+int dq_fast_variants() { return 6; }
 TileCfg dq_fast_cfg(int v) {
   const int bn = v == 2 || v == 3 ? 32 : 64, nw = v == 1 ? 4 : 8;
   const int row_halfs = v >= 3 ? 2 * kD : 2 * kLSR + kLST;
@@ -816,6 +869,9 @@ hipError_t launch_dq_variant(const BwdArgs& a, int v, int causal, hipStream_t s)
     case 2: return causal ? launch_dq_t<T, 32, 8, true, false>(a, s) : launch_dq_t<T, 32, 8, false, false>(a, s);
     case 3: return causal ? launch_dq_t<T, 32, 8, true, true>(a, s) : launch_dq_t<T, 32, 8, false, true>(a, s);
     case 4: return causal ? launch_dq_t<T, 64, 8, true, true>(a, s) : launch_dq_t<T, 64, 8, false, true>(a, s);
+    case 5:
+      if (!dq_pipe_fits(a, (int)sizeof(T))) return launch_dq_variant<T>(a, 4, causal, s);
+      return causal ? launch_dq_pipe<T, true>(a, s) : launch_dq_pipe<T, false>(a, s);
   }
   return hipErrorInvalidValue;
 }

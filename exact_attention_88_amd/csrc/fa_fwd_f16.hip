@@ -26,6 +26,7 @@
 
 #include "fa_args.h"
 #include "fa_common.h"
+#include "fa_lds.h"
 
 namespace fa {
 
@@ -498,6 +499,241 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
   }
 }
 
+
+// Pipelined kernel with buffer loads into LDS.  The method and the K-ahead
+// pipeline are those of fwd_f16_d128_pipe; what changes is how the work is
+// laid out over the instruction stream, since a wave issues only a few VALU
+// instructions per MFMA without stalling the matrix pipe and the softmax is
+// VALU-heavy:
+//   * K and V tiles are loaded straight from global memory into one swizzled
+//     copy each (no staging registers, no per-tile address arithmetic beyond a
+//     32-bit offset; keys at or past Sk read as zero and are masked);
+//   * the loop is unrolled by two, so the scores of the current and the next
+//     tile swap roles without register copies;
+//   * tile t runs as four scheduling regions, each with eight MFMAs
+//     interleaved with the LDS reads and VALU work listed for it:
+//       1: S(t+1), first 32 keys    | read V^T(t), first 32 keys  | P(t), first 32 keys
+//       2: O += P V(t), first half  | read K(t+1), second 32 keys | P(t), next 16 keys; row sum
+//       3: S(t+1), second 32 keys   | read V^T(t), second 32 keys | P(t), last 16 keys; row sum
+//       4: O += P V(t), second half | read K(t+2), first 32 keys  | mask and row max of S(t+1)
+//     with the tile's barrier between regions 3 and 4: it publishes K(t+2)
+//     and V(t+1) and frees the buffers of K(t+1) and V(t), which are refilled
+//     with K(t+3) and V(t+2) right after it.
+// Needs 31-bit byte offsets for every K and V row up to 3 tiles past Sk and a
+// row stride of at least 128 elements (checked on the host).
+template <class T, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
+  constexpr int NW = 8, BM = 32 * NW, BN = 64, TR = BN * kD;
+  __shared__ __attribute__((aligned(1024))) T smem[4 * TR];  // K0 K1 V0 V1
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
+  const int nqb = (a.Sq + BM - 1) / BM;
+  const int L = xcd_logical_block();
+  int qb = L % nqb;
+  const int bh = L / nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;
+  const int b = bh / a.H, h = bh % a.H;
+  const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
+  const T* kbase = (const T*)a.k.p + b * a.k.sb + h * a.k.sh;
+  const T* vbase = (const T*)a.v.p + b * a.v.sb + h * a.v.sh;
+  const swzl::rsrc_t rk = swzl::make_rsrc(kbase, (int)((int64_t)a.Sk * a.k.ss * (int64_t)sizeof(T)));
+  const swzl::rsrc_t rv = swzl::make_rsrc(vbase, (int)((int64_t)a.Sk * a.v.ss * (int64_t)sizeof(T)));
+
+  const int q0 = qb * BM, qi = q0 + w * 32 + c;
+
+  V8<T> qf[8];
+  {
+    const T* qrow = qbase + (int64_t)min(qi, a.Sq - 1) * a.q.ss;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const V8<T>*>(qrow + ks * 16 + g * 8);
+  }
+  // Q resident before any buffer load into LDS is issued (the compiler does
+  // not count those).
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = zero16();
+  float m = -INFINITY, lsum = 0.f, mc = 0.f;
+  const float cs = a.scale_log2;
+
+  const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
+  const int ntiles = (kend + BN - 1) / BN;
+  // Tiles [0, nfull) hold no key past the end and, causally, no key after the
+  // block's first query: their scores need no mask.
+  const int nfull = min(ntiles, (CAUSAL ? max(0, min(a.Sk, q0 + a.coff + 1)) : a.Sk) / BN);
+
+  auto kbuf = [&](int t) { return smem + (t & 1) * TR; };
+  auto vbuf = [&](int t) { return smem + 2 * TR + (t & 1) * TR; };
+  auto dma_k = [&](int t) { swzl::tile_dma<BN, NW>(rk, kbuf(t), a.k.ss, t * BN); };
+  auto dma_v = [&](int t) { swzl::tile_dma<BN, NW>(rv, vbuf(t), a.v.ss, t * BN); };
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS
+    __syncthreads();
+  };
+  // Mask tile u's scores (keys past Sk or, causally, after the row), take the
+  // row max and move the running max if it grew by more than 2^kLazy,
+  // rescaling O and the row sum.
+  auto rowmax = [&](f32x16* sc, int u) {
+    if (u >= nfull) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = u * BN + kb * 32 + crow(r, g);
+          if (key >= a.Sk || (CAUSAL && key > qi + a.coff)) sc[kb][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = max_xor32(mx);
+    // m = -inf and a finite mx give +inf > kLazy: the first scores always
+    // raise the max.  Both -inf (a row with no key yet) give NaN: no raise.
+    const bool raise = (mx - m) * cs > kLazy;
+    const float mnew = raise ? mx : m;
+    if (__any(raise)) {
+      const float alpha = raise ? fast_exp2((m - mnew) * cs) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    m = mnew;
+    mc = (mnew == -INFINITY ? 0.f : mnew) * cs;
+  };
+
+  f32x16 sa[2], sb[2];
+  V8<T> kf[8];
+  if (ntiles > 0) {
+    dma_k(0);
+    dma_k(1);
+    dma_v(0);
+    barrier();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(kbuf(0), kb * 32, ks * 2);
+      sa[kb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) sa[kb] = Mfma<T>::mma(kf[ks], qf[ks], sa[kb]);
+    }
+    __syncthreads();  // every wave has read K(0)'s buffer
+    dma_k(2);
+    dma_v(1);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(kbuf(1), 0, ks * 2);
+    rowmax(sa, 0);
+  }
+
+  // Tile t: scores S(t) in sc (row max taken), kf holds K(t+1)'s first 32
+  // keys; K(t+1) and V(t) are in LDS, K(t+2) and V(t+1) are being loaded.
+  auto step = [&](int t, f32x16* sc, f32x16* sn) {
+    const T* Kn = kbuf(t + 1);
+    const T* Vc = vbuf(t);
+    V8<T> vt[2][4], pf[2][2];
+    float rs = 0.f;
+    // ---- 1
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vt[tt][db] = swzl::frag_t_swz(Vc, 0, tt, db * 32);
+    sn[0] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) sn[0] = Mfma<T>::mma(kf[ks], qf[ks], sn[0]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[0][r] = fast_exp2(__builtin_fmaf(sc[0][r], cs, -mc));
+    pf[0][0] = frag_from_acc<T>(sc[0], 0);
+    pf[0][1] = frag_from_acc<T>(sc[0], 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- 2
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(Kn, 32, ks * 2);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] = Mfma<T>::mma(vt[tt][db], pf[0][tt], oacc[db]);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sc[1][r] = fast_exp2(__builtin_fmaf(sc[1][r], cs, -mc));
+    pf[1][0] = frag_from_acc<T>(sc[1], 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rs += sc[0][r];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- 3
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vt[tt][db] = swzl::frag_t_swz(Vc, 32, tt, db * 32);
+    sn[1] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) sn[1] = Mfma<T>::mma(kf[ks], qf[ks], sn[1]);
+#pragma unroll
+    for (int r = 8; r < 16; ++r) sc[1][r] = fast_exp2(__builtin_fmaf(sc[1][r], cs, -mc));
+    pf[1][1] = frag_from_acc<T>(sc[1], 1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rs += sc[1][r];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    lsum += rs;
+    // Publish K(t+2) and V(t+1); the buffers of K(t+1) and V(t) are free.
+    barrier();
+    dma_k(t + 3);
+    dma_v(t + 2);
+    // ---- 4
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(kbuf(t + 2), 0, ks * 2);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] = Mfma<T>::mma(vt[tt][db], pf[1][tt], oacc[db]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < ntiles) rowmax(sn, t + 1);
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < ntiles) step(t + 1, sb, sa);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no buffer load outlives the workgroup
+
+  const float ltot = add_xor32(lsum);
+  if (qi < a.Sq) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;  // no visible key: O = 0, LSE = -inf
+    T* orow = (T*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        V4<T> o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[db][r4 * 4 + e] * inv);
+        *reinterpret_cast<V4<T>*>(orow + db * 32 + r4 * 8 + g * 4) = o4;
+      }
+    if (g == 0)
+      a.lse[(int64_t)bh * a.Sq + qi] =
+          ltot > 0.f ? __builtin_fmaf(a.scale, m, fast_log2(ltot) * kLn2) : -INFINITY;
+  }
+}
+
 template <class Kernel>
 hipError_t launch_k(Kernel* k, int BM, int threads, const FwdArgs& a, hipStream_t s) {
   const int64_t grid = (((int64_t)a.Sq + BM - 1) / BM) * a.B * a.H;
@@ -519,6 +755,14 @@ hipError_t launch_plain(const FwdArgs& a, int causal, hipStream_t s) {
                 : launch_k(&fwd_f16_d128<T, BN, NW, false>, 32 * NW, NW * 64, a, s);
 }
 
+// Byte offsets of every K and V row the buffer-load kernel may address (up to
+// 3 tiles past Sk) fit in 31 bits, and rows do not overlap.
+bool fwd_dma_fits(const FwdArgs& a, int esize) {
+  const int64_t lim = (int64_t)1 << 31;
+  return a.k.ss >= kD && a.v.ss >= kD && ((int64_t)a.Sk + 3 * 64) * a.k.ss * esize < lim &&
+         ((int64_t)a.Sk + 3 * 64) * a.v.ss * esize < lim;
+}
+
 template <class T>
 hipError_t launch_variant(const FwdArgs& a, int variant, int causal, hipStream_t s) {
   switch (variant) {
@@ -526,6 +770,10 @@ hipError_t launch_variant(const FwdArgs& a, int variant, int causal, hipStream_t
     case 1: return launch_pipe<T, 64, 8, false>(a, causal, s);
     case 2: return launch_plain<T, 64, 8>(a, causal, s);
     case 3: return launch_plain<T, 64, 4>(a, causal, s);
+    case 4:
+      if (!fwd_dma_fits(a, (int)sizeof(T))) return launch_pipe<T, 64, 8, true>(a, causal, s);
+      return causal ? launch_k(&fwd_dma_d128<T, true>, 256, 512, a, s)
+                    : launch_k(&fwd_dma_d128<T, false>, 256, 512, a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -533,11 +781,14 @@ hipError_t launch_variant(const FwdArgs& a, int variant, int causal, hipStream_t
 }  // namespace
 
 // Variants (BN keys per tile, waves): pipelined 0 = (64, 8, ordered),
-// 1 = (64, 8); plain 2 = (64, 8), 3 = (64, 4).
-int fwd_fast_variants() { return 4; }
+// 1 = (64, 8); plain 2 = (64, 8), 3 = (64, 4); 4 = pipelined (64, 8) with
+// buffer loads into LDS (variant 0 runs instead where its 31-bit offsets do
+// not reach every row).
+int fwd_fast_variants() { return 5; }
 
 TileCfg fwd_fast_cfg(int v) {
   const int nw = v == 3 ? 4 : 8;
+  if (v == 4) return TileCfg{256, 64, 8, 4 * 64 * kD * 2};
   return TileCfg{32 * nw, 64, nw, 2 * 64 * (kLSK + kLSV) * 2};
 }
 

@@ -1,0 +1,106 @@
+// LDS tile layout and global -> LDS loads shared by the tuned 16-bit
+// head-dim-128 kernels (fa_fwd_f16.hip, fa_bwd_f16.hip).
+//
+// Tiles are rows of 128 16-bit elements (256 bytes) stored unpadded in an
+// XOR-swizzled layout that one copy serves for both row-wise MFMA operand
+// reads (ds_read_b128) and transposed ones (ds_read_b64_tr_b16), and are
+// filled either through registers or straight from global memory with buffer
+// loads that write LDS.
+#pragma once
+
+#include "fa_common.h"
+
+namespace fa {
+namespace swzl {
+
+constexpr int kD = 128;  // elements per tile row
+
+// Single-copy swizzled layout: unpadded 256-byte rows in which the 16-byte
+// chunk k of row r sits at chunk position k ^ swz(r).  swz(r) takes distinct
+// values on any 16 consecutive rows (so 16-row ds_read_b128 row reads and
+// full-row stores are conflict free) and, on 4 rows that start at a multiple
+// of 4, spreads 4 neighbouring chunks over all 16 chunk positions (so 4-row
+// transposed reads are conflict free).  One layout serves both read patterns.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+template <int ROWS, int NT, class T>
+__device__ __forceinline__ void tile_store_swz(const u32x4* r, T* lds) {
+  constexpr int PER = ROWS * 16 / NT;
+  static_assert(NT % 256 == 0, "every thread keeps its row residue mod 16");
+  const int row0 = (int)threadIdx.x >> 4, off = row0 * kD + (((threadIdx.x & 15) ^ swz(row0)) << 3);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) *reinterpret_cast<u32x4*>(lds + i * (NT / 16) * kD + off) = r[i];
+}
+
+// Row-wise fragment in the swizzled layout; rbase is a multiple of 16.
+template <class T>
+__device__ __forceinline__ V8<T> frag_r_swz(const T* lds, int rbase, int kchunk) {
+  const int lane = threadIdx.x & 63, r = lane & 31;
+  return *reinterpret_cast<const V8<T>*>(lds + (rbase + r) * kD +
+                                      (((kchunk + (lane >> 5)) ^ swz(r)) << 3));
+}
+
+// Transposed fragment in the swizzled layout (same lanes as frag_t); rbase is
+// a multiple of 16 and cbase of 8.
+template <class T>
+__device__ __forceinline__ V8<T> frag_t_swz(const T* lds, int rbase, int t, int cbase) {
+  const int lane = threadIdx.x & 63, g = lane >> 5, j = lane & 15;
+  const int col = ((lane >> 4) & 1) * 16 + (j & 3) * 4;
+  const int r = g * 4 + (j >> 2);
+  const int ch = (cbase >> 3) + (col >> 3);
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const T* p0 = lds + (rbase + t * 16 + r) * kD + ((ch ^ swz(r)) << 3) + (col & 7);
+  const T* p1 = lds + (rbase + t * 16 + r + 8) * kD + ((ch ^ swz(r + 8)) << 3) + (col & 7);
+  s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
+  s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1));
+  V4<T> ah = __builtin_bit_cast(V4<T>, a), bh = __builtin_bit_cast(V4<T>, b);
+  V8<T> x;
+  x[0] = ah[0]; x[1] = ah[1]; x[2] = ah[2]; x[3] = ah[3];
+  x[4] = bh[0]; x[5] = bh[1]; x[6] = bh[2]; x[7] = bh[3];
+  return x;
+}
+
+
+template <bool V> struct BoolTag { static constexpr bool value = V; };
+typedef int rsrc_t __attribute__((ext_vector_type(4)));  // buffer resource (4 SGPRs)
+
+// Raw buffer over [base, base + nbytes): stride 0, 32-bit data format.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int nbytes) {
+  const uint64_t p = (uint64_t)base;
+  rsrc_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(p & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One wave-wide 16-byte-per-lane buffer load into LDS at lds (wave-uniform):
+// lane i's bytes land at lds + 16*i.  Issued as inline assembly so that the
+// compiler does not make every later LDS read wait for it: the caller waits
+// (vmcnt(0)) before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(rsrc_t r, const void* lds, int voff) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(__attribute__((address_space(3))) const void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
+}
+
+// ROWS rows x 256 bytes into the swizzled layout at lds: ROWS/4 wave-wide
+// 1 KB loads (4 rows each) shared by the NW waves.
+template <int ROWS, int NW, class T>
+__device__ __forceinline__ void tile_dma(rsrc_t r, T* lds, int64_t ss, int row0) {
+  static_assert(ROWS % (4 * NW) == 0, "whole wave loads per wave");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < ROWS / (4 * NW); ++i) {
+    const int r0 = (i * NW + w) * 4;
+    const int row = r0 + (lane >> 4);
+    const int chunk = (lane & 15) ^ swz(row);
+    const int off = (int)((int64_t)(row0 + row) * ss * (int64_t)sizeof(T)) + chunk * 16;
+    dma16(r, lds + r0 * kD, off);
+  }
+}
+
+}  // namespace swzl
+}  // namespace fa
