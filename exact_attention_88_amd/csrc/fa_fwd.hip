@@ -253,12 +253,12 @@ const TileCfg* fwd_tile(int dtype, int D, int id) {
 
 int fwd_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
   // 16-bit, D = 128, by measurement on MI355X: the pipelined 8-wave kernel
-  // with pinned read order at S >= 4096 (by 1-3 % over the plain 8-wave
-  // kernel); for short sequences the plain 4-wave kernel (twice the
-  // workgroups, two per CU), 7-22 % faster for causal S <= 2048 and
-  // non-causal S <= 512.
+  // with buffer loads into LDS from causal S = 2048 and non-causal S = 1024
+  // up (8-15 % over the register-staged pipelined kernel); for shorter
+  // sequences the plain 4-wave kernel (twice the workgroups, two per CU),
+  // 1-14 % faster there.
   (void)Sq;
-  if (table_dt(dtype) == 0 && D == 128) return (causal ? Sk <= 2048 : Sk <= 512) ? 3 : 0;
+  if (table_dt(dtype) == 0 && D == 128) return (causal ? Sk <= 1024 : Sk <= 512) ? 3 : 4;
   return 0;
 }
 
