@@ -519,8 +519,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
 //     with the tile's barrier between regions 3 and 4: it publishes K(t+2)
 //     and V(t+1) and frees the buffers of K(t+1) and V(t), which are refilled
 //     with K(t+3) and V(t+2) right after it.
-// Needs 31-bit byte offsets for every K and V row up to 3 tiles past Sk and a
-// row stride of at least 128 elements (checked on the host).
+// Needs 31-bit byte offsets for every K and V row below Sk + 4*64 and a row
+// stride of at least 128 elements (checked on the host).
 template <class T, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
   constexpr int NW = 8, BM = 32 * NW, BN = 64, TR = BN * kD;
@@ -563,10 +563,13 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
   // block's first query: their scores need no mask.
   const int nfull = min(ntiles, (CAUSAL ? max(0, min(a.Sk, q0 + a.coff + 1)) : a.Sk) / BN);
 
-  auto kbuf = [&](int t) { return smem + (t & 1) * TR; };
-  auto vbuf = [&](int t) { return smem + 2 * TR + (t & 1) * TR; };
-  auto dma_k = [&](int t) { swzl::tile_dma<BN, NW>(rk, kbuf(t), a.k.ss, t * BN); };
-  auto dma_v = [&](int t) { swzl::tile_dma<BN, NW>(rv, vbuf(t), a.v.ss, t * BN); };
+  // Buffer of tile t's K or V: chosen by t's parity, which is a compile-time
+  // constant in the loop below (unrolled by two from an even t), so that LDS
+  // addresses are a per-lane base plus constant offsets.
+  auto kbuf = [&](int par) { return smem + (par & 1) * TR; };
+  auto vbuf = [&](int par) { return smem + 2 * TR + (par & 1) * TR; };
+  auto dma_k = [&](int t, int par) { swzl::tile_dma<BN, NW>(rk, kbuf(par), a.k.ss, t * BN); };
+  auto dma_v = [&](int t, int par) { swzl::tile_dma<BN, NW>(rv, vbuf(par), a.v.ss, t * BN); };
   auto barrier = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS
     __syncthreads();
@@ -609,9 +612,9 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
   f32x16 sa[2], sb[2];
   V8<T> kf[8];
   if (ntiles > 0) {
-    dma_k(0);
-    dma_k(1);
-    dma_v(0);
+    dma_k(0, 0);
+    dma_k(1, 1);
+    dma_v(0, 0);
     barrier();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -622,8 +625,8 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
       for (int ks = 0; ks < 8; ++ks) sa[kb] = Mfma<T>::mma(kf[ks], qf[ks], sa[kb]);
     }
     __syncthreads();  // every wave has read K(0)'s buffer
-    dma_k(2);
-    dma_v(1);
+    dma_k(2, 0);
+    dma_v(1, 1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(kbuf(1), 0, ks * 2);
     rowmax(sa, 0);
@@ -631,9 +634,10 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
 
   // Tile t: scores S(t) in sc (row max taken), kf holds K(t+1)'s first 32
   // keys; K(t+1) and V(t) are in LDS, K(t+2) and V(t+1) are being loaded.
-  auto step = [&](int t, f32x16* sc, f32x16* sn) {
-    const T* Kn = kbuf(t + 1);
-    const T* Vc = vbuf(t);
+  auto step = [&](auto parity, int t, f32x16* sc, f32x16* sn) {
+    constexpr int P = decltype(parity)::value;  // t & 1
+    const T* Kn = kbuf(P + 1);
+    const T* Vc = vbuf(P);
     V8<T> vt[2][4], pf[2][2];
     float rs = 0.f;
     // ---- 1
@@ -697,11 +701,11 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
     lsum += rs;
     // Publish K(t+2) and V(t+1); the buffers of K(t+1) and V(t) are free.
     barrier();
-    dma_k(t + 3);
-    dma_v(t + 2);
+    dma_k(t + 3, P + 1);
+    dma_v(t + 2, P);
     // ---- 4
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(kbuf(t + 2), 0, ks * 2);
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(kbuf(P), 0, ks * 2);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -710,8 +714,8 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
     if (t + 1 < ntiles) rowmax(sn, t + 1);
   };
   for (int t = 0; t < ntiles; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < ntiles) step(t + 1, sb, sa);
+    step(std::integral_constant<int, 0>{}, t, sa, sb);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1, sb, sa);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no buffer load outlives the workgroup
 
@@ -755,12 +759,13 @@ hipError_t launch_plain(const FwdArgs& a, int causal, hipStream_t s) {
                 : launch_k(&fwd_f16_d128<T, BN, NW, false>, 32 * NW, NW * 64, a, s);
 }
 
-// Byte offsets of every K and V row the buffer-load kernel may address (up to
-// 3 tiles past Sk) fit in 31 bits, and rows do not overlap.
+// Byte offsets of every K and V row the buffer-load kernel may address fit in
+// 31 bits, and rows do not overlap.  The last loads reach K tile ntiles + 2,
+// whose rows end below Sk + 4*64.
 bool fwd_dma_fits(const FwdArgs& a, int esize) {
   const int64_t lim = (int64_t)1 << 31;
-  return a.k.ss >= kD && a.v.ss >= kD && ((int64_t)a.Sk + 3 * 64) * a.k.ss * esize < lim &&
-         ((int64_t)a.Sk + 3 * 64) * a.v.ss * esize < lim;
+  return a.k.ss >= kD && a.v.ss >= kD && ((int64_t)a.Sk + 4 * 64) * a.k.ss * esize < lim &&
+         ((int64_t)a.Sk + 4 * 64) * a.v.ss * esize < lim;
 }
 
 template <class T>

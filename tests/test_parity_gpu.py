@@ -282,3 +282,35 @@ def test_long_context_sampled():
 def test_length_sweep_sampled(case):
     x, got = run_case(case)
     check_sampled(case, [(case.B - 1, case.H - 1)], x, got)
+
+
+@pytest.mark.slow
+def test_wide_row_stride_takes_the_64bit_path():
+    """Rows 64 Ki elements apart (a [S, 512, 128] store seen one head at a
+    time): byte offsets of the last key rows pass 2^31, beyond the 32-bit
+    offsets of the buffer-load kernels, so the library must run the
+    register-staged kernels with 64-bit addressing; sampled rows against the
+    oracle."""
+    fa = _fa()
+    S, stride = 16640, 512 * 128
+    case = W.Case("wide_stride_f16_causal", 1, 1, S, S, 128, "f16", True, seed=71)
+    assert (S + 3 * 64) * stride * 2 >= 1 << 31  # past every kernel's 31-bit limit
+    x = W.make_inputs(case)
+    dev = {}
+    for n, a in x.items():
+        store = torch.empty((S, 512, 128), dtype=torch.float16, device="cuda")
+        store[:, 3] = torch.from_numpy(np.ascontiguousarray(a[0, 0])).cuda()
+        dev[n] = store[:, 3].unsqueeze(0).unsqueeze(0)  # [1, 1, S, 128], row stride 65536
+        assert dev[n].stride(2) == stride
+    o = torch.full((1, 1, S, 128), float("nan"), dtype=torch.float16, device="cuda")
+    lse = U.nan_vec((1, 1, S))
+    print(f"[gpu] fwd {case.name}", flush=True)
+    fa.fa_fwd(dev["q"], dev["k"], dev["v"], True, case.scale, out=o, lse=lse)
+    dq, dk, dv = (torch.full_like(o, float("nan")) for _ in range(3))
+    delta = U.nan_vec((1, 1, S))
+    print(f"[gpu] bwd {case.name}", flush=True)
+    fa.fa_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, True, case.scale, dq=dq, dk=dk,
+              dv=dv, delta=delta)
+    torch.cuda.synchronize()
+    got = {n: U.host(t) for n, t in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items()}
+    check_sampled(case, [(0, 0)], x, got)
