@@ -533,9 +533,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   //   2: dK += dS(j-1)^T Q   | read Q^T(j)                    | P(j), first half
   //   3: dP(j) = dO V^T      | read Q rows(j+1)               | P(j), second half
   //   4: dV += P(j)^T dO     | read dO rows(j+1)              | dS(j), first half
-  // Phase 2 holds the block's last reads of cur, so the tile's barrier sits
-  // between phases 2 and 3 of its last block; phase 3 of that block reads the
-  // next tile's first rows from nxt, and so does phase 4.
+  // Phase 2 holds the block's last reads of cur; the tile's barrier sits
+  // between phases 3 and 4 of its last block (so those reads have phase 3 to
+  // land before the barrier waits for them), and phase 4 of that block reads
+  // the next tile's first Q and dO rows from nxt.
   auto tile = [&](auto masked, int t, T* cur, T* nxt) {
     constexpr bool MASKED = decltype(masked)::value;
     const int q0 = qstart + t * BM;
@@ -598,19 +599,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (qb == NQB - 1) {
-        // Every wave is done reading this buffer: refill it with the tile
-        // after next, and publish the next tile's data and row statistics.
-        store_rows(t + 1);
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's buffer loads are in LDS
-        __syncthreads();
-        if (t + 2 < ntiles) issue_tile(t + 2, cur);
-      }
       // ---- 3
       const T* nq = qb + 1 < NQB ? Qc : Qn;
       const int nr = ((qb + 1) % NQB) * 32;
+      if (qb + 1 < NQB) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(nq, nr, ks * 2);
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(nq, nr, ks * 2);
+      }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) dp = Mfma<T>::mma(of[ks], vf[ks], dp);
 #pragma unroll
@@ -626,6 +621,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (qb == NQB - 1) {
+        // Every wave is done reading this buffer (its last reads, in phase 2,
+        // had phase 3 to land): refill it with the tile after next, and
+        // publish the next tile's data and row statistics.
+        store_rows(t + 1);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's buffer loads are in LDS
+        __syncthreads();
+        if (t + 2 < ntiles) issue_tile(t + 2, cur);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(nq, nr, ks * 2);
+      }
       // ---- 4
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r_swz(nq + TR, nr, ks * 2);
