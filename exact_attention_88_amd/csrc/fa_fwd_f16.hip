@@ -577,21 +577,26 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
   // Mask tile u's scores (keys past Sk or, causally, after the row), take the
   // row max and move the running max if it grew by more than 2^kLazy,
   // rescaling O and the row sum.
-  auto rowmax = [&](f32x16* sc, int u) {
-    if (u >= nfull) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = u * BN + kb * 32 + crow(r, g);
-          if (key >= a.Sk || (CAUSAL && key > qi + a.coff)) sc[kb][r] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
+  // Max of one accumulator's 16 values as a balanced tree of v_max3 (a short
+  // dependency chain instead of 16 in a row).
+  auto max16 = [](const f32x16& x) {
+    const float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+    const float a2 = fmaxf(fmaxf(x[6], x[7]), x[8]), a3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+    const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+    return fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[15]));
+  };
+  auto mask = [&](f32x16* sc, int u) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = u * BN + kb * 32 + crow(r, g);
+        if (key >= a.Sk || (CAUSAL && key > qi + a.coff)) sc[kb][r] = -INFINITY;
+      }
+  };
+  // Move the running max to mx (this half-wave's max of the tile) if it grew
+  // by more than 2^kLazy, rescaling O and the row sum.
+  auto update = [&](float mx) {
     mx = max_xor32(mx);
     // m = -inf and a finite mx give +inf > kLazy: the first scores always
     // raise the max.  Both -inf (a row with no key yet) give NaN: no raise.
@@ -607,6 +612,10 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
     }
     m = mnew;
     mc = (mnew == -INFINITY ? 0.f : mnew) * cs;
+  };
+  auto rowmax = [&](f32x16* sc, int u) {
+    if (u >= nfull) mask(sc, u);
+    update(fmaxf(max16(sc[0]), max16(sc[1])));
   };
 
   f32x16 sa[2], sb[2];
@@ -656,7 +665,8 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- 2
@@ -675,7 +685,8 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- 3
@@ -695,10 +706,10 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    lsum += rs;
     // Publish K(t+2) and V(t+1); the buffers of K(t+1) and V(t) are free.
     barrier();
     dma_k(t + 3, P + 1);
@@ -710,6 +721,7 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] = Mfma<T>::mma(vt[tt][db], pf[1][tt], oacc[db]);
+    lsum += rs;
     __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < ntiles) rowmax(sn, t + 1);
   };
