@@ -414,9 +414,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
 //     chunk each lane fetches; rows at or past Sq fall outside the buffer's
 //     byte range and read as zero.  No staging registers are needed.
 //   * The row-wise Q and dO fragments of the next block (of the next tile,
-//     after the last block) are read while the dV and dK products of the
-//     current block run; the transposed fragments and the row statistics of a
-//     block are read while its S and dP products run.
+//     after the last block) are read under the current block's dP and dV
+//     products, a block's transposed fragments and row statistics under its
+//     S product and the previous block's dK product, and the softmax-gradient
+//     arithmetic is spread over all four products (the phases are listed
+//     above the tile body below).
 //   * One barrier per tile, inside its last block: after it the buffer just
 //     read is refilled with the tile after next, and the next tile's first
 //     fragments are read from the other buffer.
