@@ -30,8 +30,11 @@ MFMA_PEAK_F16 = 2516.6  # TFLOP/s, dense fp16, MI355X (256 CU x 4096 flop/clk x 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    # About half a second of untimed steps: the GPU needs that long under this
+    # load to reach its working clock (a first timed pass after idle reads up
+    # to a quarter slow).
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=3,
                     help="heads of the workload the CPU oracle times (bounded sample)")
