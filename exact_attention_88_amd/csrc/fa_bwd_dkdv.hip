@@ -29,42 +29,51 @@ constexpr int kLdsMax = 65536;
 
 // ----------------------------------------------------------------- preprocess
 // delta[bh, i] = sum_d dO[i, d] * O[i, d] in fp32.  G threads share a row,
-// each reading 16-byte chunks.
+// each reading 16-byte chunks; a workgroup covers NP*256/G consecutive rows
+// of one (batch, head), all of whose loads are issued before any is summed.
+constexpr int kPrePasses = 4;
+
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int CH = 16 / (int)sizeof(T);
   constexpr int G = D / CH;  // threads per row (power of two, <= 32)
-  constexpr int RPB = 256 / G;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / G;
-  const int part = threadIdx.x % G;
-  const int64_t nrows = (int64_t)a.B * a.H * a.Sq;
-  float acc = 0.f;
-  if (row < nrows) {
-    const int64_t bh = row / a.Sq;
-    const int i = (int)(row - bh * a.Sq);
-    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-    const T* orow = (const T*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)i * a.o.ss;
-    const T* drow = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh + (int64_t)i * a.dout.ss;
-    const int col = part * CH;
-    T ov[CH], dv[CH];
+  constexpr int RPP = 256 / G, NP = kPrePasses;
+  const int nblk = (a.Sq + RPP * NP - 1) / (RPP * NP);
+  const int bh = (int)blockIdx.x / nblk;
+  const int blk = (int)blockIdx.x - bh * nblk;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int part = threadIdx.x % G, col = part * CH;
+  const T* obase = (const T*)a.o.p + b * a.o.sb + h * a.o.sh;
+  const T* dbase = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh;
+  T ov[NP][CH], dv[NP][CH];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int i = min((blk * NP + p) * RPP + (int)threadIdx.x / G, a.Sq - 1);  // tail rows clamped
+    const T* orow = obase + (int64_t)i * a.o.ss;
+    const T* drow = dbase + (int64_t)i * a.dout.ss;
     if (a.vec & VEC_O) {
-      __builtin_memcpy(ov, orow + col, 16);
+      __builtin_memcpy(ov[p], orow + col, 16);
     } else {
 #pragma unroll
-      for (int e = 0; e < CH; ++e) ov[e] = orow[(int64_t)(col + e) * a.o.sd];
+      for (int e = 0; e < CH; ++e) ov[p][e] = orow[(int64_t)(col + e) * a.o.sd];
     }
     if (a.vec & VEC_DO) {
-      __builtin_memcpy(dv, drow + col, 16);
+      __builtin_memcpy(dv[p], drow + col, 16);
     } else {
 #pragma unroll
-      for (int e = 0; e < CH; ++e) dv[e] = drow[(int64_t)(col + e) * a.dout.sd];
+      for (int e = 0; e < CH; ++e) dv[p][e] = drow[(int64_t)(col + e) * a.dout.sd];
     }
-#pragma unroll
-    for (int e = 0; e < CH; ++e) acc = __builtin_fmaf((float)dv[e], (float)ov[e], acc);
   }
 #pragma unroll
-  for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < nrows && part == 0) a.delta[row] = acc;
+  for (int p = 0; p < NP; ++p) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc = __builtin_fmaf((float)dv[p][e], (float)ov[p][e], acc);
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    const int i = (blk * NP + p) * RPP + (int)threadIdx.x / G;
+    if (i < a.Sq && part == 0) a.delta[(int64_t)bh * a.Sq + i] = acc;
+  }
 }
 
 // ----------------------------------------------------------------- dK / dV
@@ -254,9 +263,8 @@ int raw_for(int dtype, int D, int id) {
 template <class T, int D>
 hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
   constexpr int G = D / (16 / (int)sizeof(T));
-  constexpr int RPB = 256 / G;
-  const int64_t rows = (int64_t)a.B * a.H * a.Sq;
-  const int64_t grid = (rows + RPB - 1) / RPB;
+  constexpr int RPB = 256 / G * kPrePasses;
+  const int64_t grid = (((int64_t)a.Sq + RPB - 1) / RPB) * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
   return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_pre_kernel<T, D>), dim3((unsigned)grid), dim3(256), args, 0, s);
