@@ -53,6 +53,28 @@ int shape_check(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int dty
   return FA_OK;
 }
 
+// Default tile of a pass: the configuration the offline sweep measured
+// fastest for this (dtype, head dim, causal, power-of-two length bucket of
+// max(Sq, Sk), clamped to 128..16384) -- "Triton FlashAttention": block sizes
+// per power-of-two length bucket -- else the pass's built-in rule.
+#include "fa_tile_table.inc"
+
+int tile_default(int pass, int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
+  int (*rule)(int, int, int64_t, int64_t, int) = pass == FA_PASS_FWD      ? fa::fwd_tile_default
+                                               : pass == FA_PASS_BWD_DKDV ? fa::dkdv_tile_default
+                                                                          : fa::dq_tile_default;
+  int (*count)(int, int) = pass == FA_PASS_FWD      ? fa::fwd_tile_count
+                           : pass == FA_PASS_BWD_DKDV ? fa::dkdv_tile_count
+                                                      : fa::dq_tile_count;
+  const int di = D == 16 ? 0 : D == 32 ? 1 : D == 64 ? 2 : 3;
+  const int64_t len = Sq > Sk ? Sq : Sk;
+  int bi = 0;
+  while (bi < 7 && ((int64_t)128 << bi) < len) ++bi;
+  const int id = kSweptTiles[pass][dtype][di][causal ? 1 : 0][bi];
+  if (id >= 0 && id < count(dtype, D)) return id;
+  return rule(dtype, D, Sq, Sk, causal);
+}
+
 int fwd_impl(int tile, const void* q, const int64_t* qs, const void* k, const int64_t* ks,
              const void* v, const int64_t* vs, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
              int64_t D, int causal, float scale, int dtype, void* out, const int64_t* os,
@@ -70,7 +92,7 @@ int fwd_impl(int tile, const void* q, const int64_t* qs, const void* k, const in
     return FA_ERR_ALIAS;
   const int dt = dtype;
   const int d = (int)D;
-  if (tile < 0) tile = fa::fwd_tile_default(dt, d, Sq, Sk, causal);
+  if (tile < 0) tile = tile_default(FA_PASS_FWD, dt, d, Sq, Sk, causal);
   if (tile >= fa::fwd_tile_count(dt, d)) return FA_ERR_TILE;
   const int es = esize(dt);
   FwdArgs a;
@@ -123,8 +145,8 @@ int bwd_impl(int stage, int tile_kv, int tile_q, const void* q, const int64_t* q
   }
   const int dt = dtype;
   const int d = (int)D;
-  if (tile_kv < 0) tile_kv = fa::dkdv_tile_default(dt, d, Sq, Sk, causal);
-  if (tile_q < 0) tile_q = fa::dq_tile_default(dt, d, Sq, Sk, causal);
+  if (tile_kv < 0) tile_kv = tile_default(FA_PASS_BWD_DKDV, dt, d, Sq, Sk, causal);
+  if (tile_q < 0) tile_q = tile_default(FA_PASS_BWD_DQ, dt, d, Sq, Sk, causal);
   if (tile_kv >= fa::dkdv_tile_count(dt, d) || tile_q >= fa::dq_tile_count(dt, d))
     return FA_ERR_TILE;
   static const int64_t zs[4] = {0, 0, 0, 1};
@@ -258,12 +280,10 @@ int fa_tile_info(int pass, int dtype, int64_t D, int tile_id, int64_t info[4]) {
 int fa_tile_default(int pass, int dtype, int64_t D, int64_t Sq, int64_t Sk, int causal) {
   if (!valid_dtype(dtype)) return FA_ERR_DTYPE;
   if (!valid_d(D)) return FA_ERR_SHAPE;
-  switch (pass) {
-    case FA_PASS_FWD: return fa::fwd_tile_default(dtype, (int)D, Sq, Sk, causal);
-    case FA_PASS_BWD_DKDV: return fa::dkdv_tile_default(dtype, (int)D, Sq, Sk, causal);
-    case FA_PASS_BWD_DQ: return fa::dq_tile_default(dtype, (int)D, Sq, Sk, causal);
-  }
-  return FA_ERR_TILE;
+  if (pass < FA_PASS_FWD || pass > FA_PASS_BWD_DQ) return FA_ERR_TILE;
+  if (causal < 0 || causal > 2) return FA_ERR_CAUSAL;
+  if (Sq < 0 || Sk < 0) return FA_ERR_SHAPE;
+  return tile_default(pass, dtype, (int)D, Sq, Sk, causal);
 }
 
 const char* fa_status_string(int status) {

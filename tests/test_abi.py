@@ -160,3 +160,39 @@ def test_tile_tables_fit_lds_and_are_consistent(dtype, D):
         assert 0 <= d < n
     assert fa.fa_tile_count(0, dtype, 48) == 0
     assert fa.fa_tile_count(9, dtype, D) == 0
+
+
+def _swept_table():
+    """kSweptTiles from the generated table, as a nested list."""
+    import os
+    import re
+    path = os.path.join(os.path.dirname(fa.__file__), "csrc", "fa_tile_table.inc")
+    body = re.sub(r"//[^\n]*", "", open(path).read()).split("=", 1)[1]
+    nums = [int(x) for x in re.findall(r"-?\d+", body)]
+    assert len(nums) == 3 * 3 * 4 * 2 * 8
+    it = iter(nums)
+    return [[[[[next(it) for _ in range(8)] for _ in range(2)] for _ in range(4)] for _ in range(3)]
+            for _ in range(3)]
+
+
+@pytest.mark.parametrize("pass_id", [0, 1, 2])
+def test_tile_default_follows_the_swept_table(pass_id):
+    """The default configuration is the sweep's pick for the power-of-two
+    bucket of max(Sq, Sk), clamped to 128..16384 (lengths between two buckets
+    take the larger one), for every dtype, head dim and causal mode."""
+    table = _swept_table()
+    for dtype in (0, 1, 2):
+        for di, D in enumerate((16, 32, 64, 128)):
+            n = fa.fa_tile_count(pass_id, dtype, D)
+            for causal in (0, 1, 2):
+                for bi in range(8):
+                    b = 128 << bi
+                    want = table[pass_id][dtype][di][1 if causal else 0][bi]
+                    lens = [(b, b), (b // 2 + 1, b), (b, 7)] if bi else [(1, 1), (100, 128), (128, 3)]
+                    if bi == 7:
+                        lens.append((3 * b, b))  # longer than the last bucket: clamped to it
+                    for Sq, Sk in lens:
+                        d = fa.fa_tile_default(pass_id, dtype, D, Sq, Sk, causal)
+                        assert 0 <= d < n
+                        if want >= 0:
+                            assert d == want, (pass_id, dtype, D, causal, Sq, Sk, d, want)
