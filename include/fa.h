@@ -140,7 +140,12 @@ int fa_bwd(const void* q, const int64_t q_strides[4],
  * {block_m, block_n, waves, lds_bytes} of configuration `tile_id` into
  * info[4] and returns FA_OK or FA_ERR_TILE.  fa_tile_default returns the
  * id that fa_fwd / fa_bwd choose for the given problem (or a negative
- * fa_status).
+ * fa_status: FA_ERR_DTYPE, FA_ERR_SHAPE for an unsupported D or a negative
+ * length, FA_ERR_CAUSAL, FA_ERR_TILE for an unknown pass): the configuration
+ * measured fastest on MI355X for the pass, dtype, head dim, causal flag
+ * (bottom-right counts as causal) and the power-of-two bucket of
+ * max(Sq, Sk), clamped to 128..16384 (a compiled-in table written by the
+ * offline sweep exact_attention_88_amd/tile_sweep.py).
  */
 int fa_tile_count(int pass, int dtype, int64_t D);
 int fa_tile_info(int pass, int dtype, int64_t D, int tile_id, int64_t info[4]);
