@@ -120,7 +120,7 @@ def _rising_inputs(case, growth):
 
 RISING = [(dname, D, causal, t) for dname, D in (("f16", 128), ("bf16", 128), ("f16", 64),
                                                  ("f32", 64))
-          for causal in (False, True) for t in range(4 if D == 128 and dname != "f32" else 1)]
+          for causal in (False, True) for t in range(5 if D == 128 and dname != "f32" else 1)]
 
 
 @pytest.mark.parametrize("dname,D,causal,t", RISING,
