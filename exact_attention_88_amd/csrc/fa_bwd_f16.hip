@@ -21,6 +21,8 @@
 // the wave's 32 rows live in registers, K and V stream (K in both layouts).
 // dK/dV kernel: one workgroup per 32*waves keys; K and V of the wave's 32 keys
 // live in registers, Q and dO stream in both layouts with LSE and delta.
+#include <type_traits>
+
 #include "fa_args.h"
 #include "fa_common.h"
 #include "fa_lds.h"
@@ -708,10 +710,13 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
 // ------------------------------------------------ dQ, buffer loads into LDS
 // dq_f16_d128 with 64-key tiles in the swizzled layout and 8 waves, with the
 // K and V tiles loaded straight into LDS by buffer loads (no staging
-// registers; keys at or past Sk read as zero and are masked) and the dP^T
-// accumulators starting from -delta, so that dS = P * (dP - delta) is one
-// multiply per element.  The registers the staging held pay for the -delta
-// start.  Needs the 31-bit offsets the dK/dV kernel needs, for K and V.
+// registers; keys at or past Sk read as zero and are masked).  Each 32-key
+// block runs its 24 MFMAs (S, dP, dQ) in a pinned order with every LDS
+// fragment read four MFMAs ahead of its use; the registers that read-ahead
+// needs come from subtracting delta after the dP product (one more VALU
+// instruction per element) instead of holding it splatted as the dP start
+// value, and from a compile-time buffer parity (immediate LDS offsets).
+// Needs the 31-bit offsets the dK/dV kernel needs, for K and V.
 template <class T, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
   constexpr int NW = 8, BM = 32 * NW, BN = 64, NT = NW * 64, NKB = BN / 32;
@@ -719,7 +724,10 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) T smem[2 * BUF];
   (void)NT;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
+  // The wave index in a scalar register: the per-wave causal skips and mask
+  // tests below are then uniform branches.
+  const int lane = threadIdx.x & 63, g = lane >> 5, c = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int nqb = (a.Sq + BM - 1) / BM;
   const int L = xcd_logical_block();
   int qb = L % nqb;
@@ -752,9 +760,6 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
   // Row data resident before any buffer load into LDS is issued (the compiler
   // does not count those).
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  f32x16 ndl;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) ndl[r] = -dlt;
 
   f32x16 dq[4];
 #pragma unroll
@@ -772,9 +777,13 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Tile t reads buffer t & 1, a compile-time constant below (the loop is
+  // unrolled by two from an even t), so LDS fragment addresses are per-lane
+  // bases plus immediate offsets.
+  auto tile = [&](auto parity, int t) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
     const int k0 = t * BN;
-    const T* Kr = smem + (t & 1) * BUF;
+    const T* Kr = smem + P * BUF;
     const T* Vr = Kr + TR;
     // The other buffer was last read in tile t-1, before the barrier below.
     if (t + 1 < ntiles) issue_tile(t + 1);
@@ -782,16 +791,30 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
     for (int kb = 0; kb < NKB; ++kb) {
       const int ks0 = k0 + kb * 32;
       if (CAUSAL && ks0 > qw + a.coff + 31) continue;
-      V8<T> kf[8], vf[8];
+      // Products in a fixed order, each LDS fragment read issued four MFMAs
+      // ahead of its use: K rows for S, then V rows for dP, then the first
+      // half of transposed K for dQ; only VALU, SALU and global loads may be
+      // scheduled across the pinned order.
+      constexpr int kPin = 0x2 | 0x4 | 0x20;
+      V8<T> kf[8], vf[8], kt[2][4];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) kf[ks] = frag_r_swz(Kr, kb * 32, ks * 2);
+      for (int ks = 0; ks < 4; ++ks) kf[ks] = frag_r_swz(Kr, kb * 32, ks * 2);
+      __builtin_amdgcn_sched_barrier(kPin);
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) vf[ks] = frag_r_swz(Vr, kb * 32, ks * 2);
-      f32x16 s = zero16(), dp = ndl;
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks + 4 < 8) kf[ks + 4] = frag_r_swz(Kr, kb * 32, (ks + 4) * 2);
+        else vf[ks - 4] = frag_r_swz(Vr, kb * 32, (ks - 4) * 2);
+        s = Mfma<T>::mma(kf[ks], qf[ks], s);
+        __builtin_amdgcn_sched_barrier(kPin);
+      }
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s = Mfma<T>::mma(kf[ks], qf[ks], s);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) dp = Mfma<T>::mma(vf[ks], df[ks], dp);
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks + 4 < 8) vf[ks + 4] = frag_r_swz(Vr, kb * 32, (ks + 4) * 2);
+        else kt[0][ks - 4] = frag_t_swz(Kr, kb * 32, 0, (ks - 4) * 32);
+        dp = Mfma<T>::mma(vf[ks], df[ks], dp);
+        __builtin_amdgcn_sched_barrier(kPin);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = fast_exp2(__builtin_fmaf(s[r], cs, -lse2));
       // Masks only on the diagonal block and the ragged key tail.
@@ -803,19 +826,26 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = s[r] * dp[r];
+      for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - dlt);
+      const V8<T> sf0 = cvt8<T>(s, 0), sf1 = cvt8<T>(s, 1);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        V8<T> kt[4];
+      for (int db = 0; db < 4; ++db) {
+        kt[1][db] = frag_t_swz(Kr, kb * 32, 1, db * 32);
+        dq[db] = Mfma<T>::mma(kt[0][db], sf0, dq[db]);
+        __builtin_amdgcn_sched_barrier(kPin);
+      }
 #pragma unroll
-        for (int db = 0; db < 4; ++db) kt[db] = frag_t_swz(Kr, kb * 32, tt, db * 32);
-        const V8<T> sf = cvt8<T>(s, tt);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dq[db] = Mfma<T>::mma(kt[db], sf, dq[db]);
+      for (int db = 0; db < 4; ++db) {
+        dq[db] = Mfma<T>::mma(kt[1][db], sf1, dq[db]);
+        __builtin_amdgcn_sched_barrier(kPin);
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's buffer loads are in LDS
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < ntiles) tile(std::integral_constant<int, 1>{}, t + 1);
   }
 
   if (valid) {
