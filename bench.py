@@ -86,11 +86,13 @@ def time_path(fa, torch, case, dev, steps, warmup):
         fa.fa_fwd(q, k, v, case.causal, sc, out=o, lse=lse)
         if ev is not None:
             ev[1].record()
-        for stage in (0, 1, 2):
+        # rowsum(dO.O) (nothing where the dQ kernel forms it), dQ, dK/dV: the
+        # order fa_bwd runs them in.
+        for j, stage in enumerate((0, 2, 1)):
             fa.fa_bwd_stage(stage, -1, q, k, v, o, do, lse, case.causal, sc, dq=dq, dk=dk, dv=dv,
                             delta=delta)
             if ev is not None:
-                ev[2 + stage].record()
+                ev[2 + j].record()
 
     for _ in range(warmup):
         step()
@@ -101,7 +103,7 @@ def time_path(fa, torch, case, dev, steps, warmup):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+    names = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv")
     per = {n: [] for n in names}
     for ev in evs:
         for j, n in enumerate(names):

@@ -175,13 +175,17 @@ int bwd_impl(int stage, int tile_kv, int tile_q, const void* q, const int64_t* q
            (vec_ok(dout, dos, es) ? fa::VEC_DO : 0) | (vec_ok(dq, dqs, es) ? fa::VEC_DQ : 0);
   a.vec = vec;
   a.coff = causal == 2 ? (int)(Sk - Sq) : 0;
+  // delta = rowsum(dO o O) comes from its own kernel (stage 0) or, where the
+  // chosen dQ kernel can form it from the rows it holds, from the dQ kernel
+  // (stage 2), which then runs first; the dK/dV kernel (stage 1) reads it.
+  a.fuse_delta = has_q && fa::dq_can_fuse_delta(a, dt, d, tile_q) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (has_q && (stage < 0 || stage == 0)) e = fa::launch_bwd_pre(a, dt, d, s);
-  if (e == hipSuccess && Sk > 0 && (stage < 0 || stage == 1))
-    e = fa::launch_dkdv(a, dt, d, causal ? 1 : 0, tile_kv, s);
+  if (has_q && !a.fuse_delta && (stage < 0 || stage == 0)) e = fa::launch_bwd_pre(a, dt, d, s);
   if (e == hipSuccess && has_q && (stage < 0 || stage == 2))
     e = fa::launch_dq(a, dt, d, causal ? 1 : 0, tile_q, s);
+  if (e == hipSuccess && Sk > 0 && (stage < 0 || stage == 1))
+    e = fa::launch_dkdv(a, dt, d, causal ? 1 : 0, tile_kv, s);
   return hip_status(e);
 }
 
@@ -242,7 +246,9 @@ int fa_bwd_stage(int stage, int tile_id, const void* q, const int64_t q_strides[
                  void* stream) {
   if (stage < 0 || stage > 2) return FA_ERR_TILE;
   if (tile_id < -1) return FA_ERR_TILE;
-  return bwd_impl(stage, stage == 1 ? tile_id : -1, stage == 2 ? tile_id : -1, q, q_strides, k,
+  // Stages 0 and 2 take the dQ tile: it decides whether delta comes from its
+  // own kernel (stage 0) or from the dQ kernel (stage 2).
+  return bwd_impl(stage, stage == 1 ? tile_id : -1, stage != 1 ? tile_id : -1, q, q_strides, k,
                   k_strides, v, v_strides, o, o_strides, dout, dout_strides, lse, B, H, Sq, Sk,
                   D, causal, scale, dtype, delta_ws, dq, dq_strides, dk, dk_strides, dv,
                   dv_strides, stream);

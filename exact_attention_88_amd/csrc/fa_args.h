@@ -36,6 +36,7 @@ struct BwdArgs {
   float scale_log2;  // scale * log2(e)
   int vec;
   int coff;          // causal: query i sees keys j <= i + coff (0 top-left, Sk - Sq bottom-right)
+  int fuse_delta;    // the dQ kernel computes delta = rowsum(dO o O) itself and writes it
 };
 
 struct TileCfg {
@@ -71,6 +72,10 @@ int dq_tile_count(int dtype, int D);
 const TileCfg* dq_tile(int dtype, int D, int id);
 int dq_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal);
 hipError_t launch_dq(const BwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s);
+// Whether launch_dq with this tile runs a kernel that can compute delta itself
+// (the buffer-load dQ kernel, which holds each query row's dO and reads its O
+// row), so that the separate rowsum(dO o O) kernel is not needed.
+bool dq_can_fuse_delta(const BwdArgs& a, int dtype, int D, int tile);
 
 hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int D, hipStream_t s);
 
@@ -78,6 +83,7 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int D, hipStream_t s);
 int dq_fast_variants();
 TileCfg dq_fast_cfg(int variant);
 hipError_t launch_dq_fast(const BwdArgs& a, int variant, int dtype, int causal, hipStream_t s);
+bool dq_fast_fuses_delta(const BwdArgs& a, int variant, int dtype);
 int dkdv_fast_variants();
 TileCfg dkdv_fast_cfg(int variant);
 hipError_t launch_dkdv_fast(const BwdArgs& a, int variant, int dtype, int causal, hipStream_t s);

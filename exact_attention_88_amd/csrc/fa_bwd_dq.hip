@@ -230,6 +230,12 @@ int dq_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
   return 0;
 }
 
+bool dq_can_fuse_delta(const BwdArgs& a, int dtype, int D, int tile) {
+  if (tile >= fast_count(dtype, D)) return false;
+  const int need = VEC_Q | VEC_K | VEC_V | VEC_DO | VEC_DQ | VEC_O;
+  return (a.vec & need) == need && dq_fast_fuses_delta(a, tile, dtype);
+}
+
 hipError_t launch_dq(const BwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s) {
   const int nf = fast_count(dtype, D);
   if (tile < nf) {

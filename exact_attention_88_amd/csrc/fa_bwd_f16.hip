@@ -742,8 +742,8 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
   const bool valid = qi < a.Sq;
 
   V8<T> qf[8], df[8];
+  const int qc = min(qi, a.Sq - 1);
   {
-    const int qc = min(qi, a.Sq - 1);
     const T* qrow = (const T*)a.q.p + b * a.q.sb + h * a.q.sh + (int64_t)qc * a.q.ss;
     const T* drow =
         (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh + (int64_t)qc * a.dout.ss;
@@ -756,7 +756,26 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
   // Rows past the end, and rows with no visible key (LSE = -inf), get P = 0.
   const float lse_n = valid ? a.lse[(int64_t)bh * a.Sq + qi] : INFINITY;
   const float lse2 = lse_n == -INFINITY ? INFINITY : lse_n * kLog2e;
-  const float dlt = valid ? a.delta[(int64_t)bh * a.Sq + qi] : 0.f;
+  float dlt;
+  if (a.fuse_delta) {
+    // delta = rowsum(dO o O) of this row ("Triton FlashAttention": the
+    // backward's preprocess), formed here from the dO fragments this lane
+    // holds and the matching half of the O row, the other half coming from
+    // lane c + 32; written for the dK/dV kernel, which runs after this one.
+    const T* orow = (const T*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qc * a.o.ss;
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const V8<T> of = *reinterpret_cast<const V8<T>*>(orow + ks * 16 + g * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)df[ks][e], (float)of[e], acc);
+    }
+    dlt = acc + xor32(acc);
+    if (valid && g == 0) a.delta[(int64_t)bh * a.Sq + qi] = dlt;
+    if (!valid) dlt = 0.f;
+  } else {
+    dlt = valid ? a.delta[(int64_t)bh * a.Sq + qi] : 0.f;
+  }
   // Row data resident before any buffer load into LDS is issued (the compiler
   // does not count those).
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -912,6 +931,11 @@ hipError_t launch_dq_variant(const BwdArgs& a, int v, int causal, hipStream_t s)
       return causal ? launch_dq_pipe<T, true>(a, s) : launch_dq_pipe<T, false>(a, s);
   }
   return hipErrorInvalidValue;
+}
+// Variant 5 runs dq_pipe_d128 where its 31-bit offsets reach every row: that
+// kernel can form delta itself.
+bool dq_fast_fuses_delta(const BwdArgs& a, int v, int dtype) {
+  return v == 5 && dq_pipe_fits(a, dtype == 1 ? 4 : 2);
 }
 hipError_t launch_dq_fast(const BwdArgs& a, int v, int dtype, int causal, hipStream_t s) {
   if (dtype == 2) return launch_dq_variant<bf16_t>(a, v, causal, s);

@@ -279,7 +279,9 @@ def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, dq=None, dk=None, dv
 
 def fa_bwd_stage(stage, tile_id, q, k, v, o, dout, lse, causal=False, scale=None, dq=None,
                  dk=None, dv=None, delta=None):
-    """One backward kernel alone (0 = rowsum(dO.O), 1 = dK/dV, 2 = dQ)."""
+    """One backward kernel alone: 0 = rowsum(dO.O) (nothing where the dQ kernel
+    forms it; ``tile_id`` is then the dQ tile), 2 = dQ, 1 = dK/dV.  Stages
+    0, 2, 1 in that order are exactly ``fa_bwd_tile``."""
     t = (tile_id, tile_id)
     return fa_bwd_tile(t[0], t[1], q, k, v, o, dout, lse, causal, scale, dq, dk, dv, delta,
                        _stage=stage)

@@ -182,10 +182,14 @@ int fa_bwd_tile(int dkdv_tile_id, int dq_tile_id,
 /*
  * fa_bwd_stage -- one of the three backward kernels alone, with the same
  * arguments as fa_bwd_tile: stage 0 = the rowsum(dO.O) preprocess (writes
- * delta_ws; `tile_id` ignored), 1 = the dK/dV kernel (reads delta_ws, writes
- * dk, dv; q/o/dout/lse/dq may be NULL when Sq == 0), 2 = the dQ kernel
- * (reads delta_ws, writes dq).  Running stages 0, 1, 2 in order on one stream
- * is exactly fa_bwd_tile.  For per-kernel timing and profiling.
+ * delta_ws; `tile_id` is the dQ tile stage 2 will run, -1 for the default),
+ * 2 = the dQ kernel (writes dq), 1 = the dK/dV
+ * kernel (reads delta_ws, writes dk, dv; q/o/dout/lse/dq may be NULL when
+ * Sq == 0).  Where the chosen dQ kernel can form delta from the rows it
+ * holds (16-bit, D = 128, 16-byte-aligned rows: the default there), stage 0
+ * launches nothing and stage 2 writes delta_ws itself; otherwise stage 2
+ * reads it.  Running stages 0, 2, 1 in that order on one stream is exactly
+ * fa_bwd_tile.  For per-kernel timing and profiling.
  */
 int fa_bwd_stage(int stage, int tile_id,
                  const void* q, const int64_t q_strides[4],
