@@ -2,8 +2,9 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
 One step = the whole path over one batch of resident synthetic inputs:
-fa_fwd (forward kernel) followed by the three backward kernels (rowsum(dO.O),
-dK/dV, dQ), each launched through the C ABI on torch's current stream.
+fa_fwd (forward kernel) followed by the backward kernels (dQ, which forms
+rowsum(dO.O) itself on this path, then dK/dV), each launched through the C ABI
+on torch's current stream.
 
 Default workload: long-context causal fp16 attention, B=1, H=16,
 S=16384, D=128, Q/K/V/dO iid N(0,1) rounded to fp16.

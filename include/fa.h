@@ -113,7 +113,10 @@ int fa_fwd(const void* q, const int64_t q_strides[4],
  * q, k, v, o (= fa_fwd's out), dO and lse (= fa_fwd's lse for the same
  * inputs) are read; delta_ws is a caller-owned float32 [B,H,Sq] workspace
  * that is overwritten (it holds delta afterwards); dq [B,H,Sq,D], dk and dv
- * [B,H,Sk,D] are overwritten.  The three kernels run in order on `stream`.
+ * [B,H,Sk,D] are overwritten.  The kernels run in order on `stream`: the
+ * rowsum, the dQ kernel, the dK/dV kernel; where the dQ kernel can form delta
+ * from the query rows it holds (16-bit, D = 128, 16-byte-aligned rows) there
+ * is no separate rowsum launch and the dQ kernel writes delta_ws.
  */
 int fa_bwd(const void* q, const int64_t q_strides[4],
            const void* k, const int64_t k_strides[4],
@@ -180,7 +183,7 @@ int fa_bwd_tile(int dkdv_tile_id, int dq_tile_id,
                 void* stream);
 
 /*
- * fa_bwd_stage -- one of the three backward kernels alone, with the same
+ * fa_bwd_stage -- one of the backward kernels alone, with the same
  * arguments as fa_bwd_tile: stage 0 = the rowsum(dO.O) preprocess (writes
  * delta_ws; `tile_id` is the dQ tile stage 2 will run, -1 for the default),
  * 2 = the dQ kernel (writes dq), 1 = the dK/dV
