@@ -15,7 +15,8 @@ from PyTorch to Triton", the benchmark harness's attn_flops); forward+backward
 reports the dominant kernel against the dense fp16 MFMA peak of MI355X.
 
 Beside the headline figure the line carries: the same step in bfloat16, the
-peak memory beyond the inputs of one autograd forward + backward, the length
+peak memory beyond the inputs of one autograd forward + backward, the measured
+dense fp16 MFMA and v_exp_f32 rates of the device (library probes), the length
 sweep (S = 512 ... 16384 with B = 16384/S, causal and not, forward and
 forward+backward TFLOP/s and fraction of peak), the CPU oracle timed on a
 bounded sample of the workload, and the pages' own T4 figures as context.
@@ -136,6 +137,32 @@ def length_sweep(fa, torch, steps, warmup):
                     "ms_per_step": round(wall / steps * 1e3, 4),
                     "kernel_ms": {n: round(v, 4) for n, v in avg.items()}})
     cached.clear()
+    return out
+
+
+def probe_rates(fa, torch):
+    """Measured ceilings on this device: dense fp16 MFMA TFLOP/s and v_exp_f32
+    exponentials per second (the library's probes, timed with HIP events on
+    the stream they run on after a warm-up launch)."""
+    n = fa.fa_probe_threads()
+    sink = torch.empty(n, device="cuda")
+    out = {}
+    for kind, iters in ((0, 4000), (1, 20000)):
+        fa.fa_probe(kind, iters, sink)
+        best = float("inf")
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fa.fa_probe(kind, iters, sink)
+            e1.record()
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        if kind == 0:
+            tf = (n // 64) * iters * 4 * 32768 / best / 1e12
+            out["mfma_f16_tflops"] = round(tf, 1)
+            out["mfma_f16_frac_of_peak"] = round(tf / MFMA_PEAK_F16, 4)
+        else:
+            out["exp2_per_s"] = float(f"{n * iters * 8 / best:.4g}")
     return out
 
 
@@ -301,6 +328,13 @@ def main():
                         "kernel_ms": {n: round(v, 4) for n, v in bavg.items()}}
         del bdev
     line["memory"] = peak_memory(torch, case, dev)
+    # Secondary ceilings: the measured MFMA rate, and the exponential rate
+    # against the step's exponentials (one per visible score in the forward,
+    # the dQ and the dK/dV kernels: 3 x B*H*Sq*Sk, halved when causal).
+    probes = probe_rates(fa, torch)
+    n_exp = 3 * case.B * case.H * case.Sq * case.Sk / (2 if case.causal else 1)
+    probes["exp2_floor_ms_per_step"] = round(n_exp / probes["exp2_per_s"] * 1e3, 4)
+    line["probes"] = probes
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, x, args.cpu_heads)
     if not args.no_length_sweep or args.sweep:

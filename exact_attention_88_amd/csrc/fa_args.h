@@ -79,6 +79,10 @@ bool dq_can_fuse_delta(const BwdArgs& a, int dtype, int D, int tile);
 
 hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int D, hipStream_t s);
 
+// Measurement probes (fa_probe.hip): kind 0 = fp16 MFMA, 1 = v_exp_f32.
+int probe_workgroups();
+hipError_t launch_probe(int kind, int iters, float* sink, hipStream_t s);
+
 // Tuned fp16 / head-dim-128 backward kernels (fa_bwd_f16.hip).
 int dq_fast_variants();
 TileCfg dq_fast_cfg(int variant);

@@ -196,3 +196,11 @@ def test_tile_default_follows_the_swept_table(pass_id):
                         assert 0 <= d < n
                         if want >= 0:
                             assert d == want, (pass_id, dtype, D, causal, Sq, Sk, d, want)
+
+
+def test_probe_rejects_bad_arguments_before_any_launch():
+    sink = ctypes.c_void_p(FAKE)
+    assert lib.fa_probe(2, 10, sink, None) == -2     # unknown kind
+    assert lib.fa_probe(-1, 10, sink, None) == -2
+    assert lib.fa_probe(0, 0, sink, None) == -2      # no iterations
+    assert lib.fa_probe(1, 10, None, None) == -1     # no sink
