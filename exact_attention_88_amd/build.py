@@ -37,10 +37,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
-# Translation units holding the tuned kernels: any scratch (spilled or
-# stack-allocated) memory in them is a build error, since a spill inside their
-# tile loops costs more than the tuning gains.
-NO_SCRATCH = {"fa_fwd_f16.hip", "fa_bwd_f16.hip"}
+# Any kernel that uses scratch (spilled or stack-allocated) memory is a build
+# error: spilling tile configurations are pruned from the tile tables.  The
+# exceptions are the generic fp32 head-dim-128 backward kernels, where every
+# candidate spills and the one that spills least is kept (mangled-name
+# fragments of the allowed instantiations).
+ALLOWED_SCRATCH = ("11dkdv_kernelIfLi128ELi32ELi4E", "9dq_kernelIfLi128ELi32ELi4ELb0E")
 
 
 def _scratch_kernels(remarks: str):
@@ -58,16 +60,15 @@ def _scratch_kernels(remarks: str):
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-    if src in NO_SCRATCH:
-        cmd.append("-Rpass-analysis=kernel-resource-usage")
+    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj,
+           "-Rpass-analysis=kernel-resource-usage"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    if src in NO_SCRATCH:
-        bad = _scratch_kernels(res.stderr)
-        if bad:
-            raise RuntimeError(f"{src}: tuned kernels use scratch memory: {bad}")
+    bad = [(k, n) for k, n in _scratch_kernels(res.stderr)
+           if not any(frag in k for frag in ALLOWED_SCRATCH)]
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch memory: {bad}")
     return obj
 
 

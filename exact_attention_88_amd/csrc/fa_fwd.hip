@@ -32,8 +32,12 @@ constexpr int lds_bytes(int esize, int D, int bn) {
 }
 constexpr FwdTile tile_at(int dt, int i) { return dt == 0 ? kTilesH[i] : kTilesF[i]; }
 constexpr int num_tiles_raw(int dt) { return dt == 0 ? kNumH : kNumF; }
+// A tile survives if its LDS fits and its kernel compiles without spilling
+// (measured with hipcc for gfx950: the fp32 head-dim-128 kernel with 8 waves
+// spills; the build fails on any other kernel that uses scratch memory).
 constexpr bool tile_ok(int dt, int D, int i) {
-  return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bn) <= kLdsMax;
+  return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bn) <= kLdsMax &&
+         !(dt == 1 && D == 128 && tile_at(dt, i).nw == 8);
 }
 // Map compact id (among fitting tiles) -> raw index, or -1.
 constexpr int raw_index(int dt, int D, int id) {
