@@ -641,6 +641,13 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
     rowmax(sa, 0);
   }
 
+  // Causal: the last key tile any row of this wave sees.  Past it the wave
+  // has nothing to compute (its probabilities of later tiles are all zero),
+  // so for those tiles it only joins the barrier and issues its share of the
+  // loads (the second loop below).
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int ulast = CAUSAL ? (q0 + wv * 32 + 31 + a.coff) / BN : 0x7fffffff;
+
   // Tile t: scores S(t) in sc (row max taken), kf holds K(t+1)'s first 32
   // keys; K(t+1) and V(t) are in LDS, K(t+2) and V(t+1) are being loaded.
   auto step = [&](auto parity, int t, f32x16* sc, f32x16* sn) {
@@ -725,9 +732,15 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < ntiles) rowmax(sn, t + 1);
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  const int tc = CAUSAL ? min(ntiles, max(0, ulast + 1)) : ntiles;
+  for (int t = 0; t < tc; t += 2) {
     step(std::integral_constant<int, 0>{}, t, sa, sb);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1, sb, sa);
+    if (t + 1 < tc) step(std::integral_constant<int, 1>{}, t + 1, sb, sa);
+  }
+  for (int t = tc; t < ntiles; ++t) {  // causal: past this wave's last visible key
+    barrier();
+    dma_k(t + 3, t + 1);
+    dma_v(t + 2, t);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no buffer load outlives the workgroup
 
