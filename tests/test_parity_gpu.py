@@ -314,6 +314,16 @@ def test_long_context_sampled():
 
 
 @pytest.mark.slow
+def test_long_context_bf16_sampled():
+    """The long workload in bfloat16 (the bench's second figure): the same
+    draws rounded to bfloat16, sampled rows against the oracle."""
+    import dataclasses
+    case = dataclasses.replace(W.long_case(), name="long_bf16_causal", dtype="bf16")
+    x, got = run_case(case)
+    check_sampled(case, [(0, 3), (0, 12)], x, got, seed=1)
+
+
+@pytest.mark.slow
 @pytest.mark.parametrize("case", W.sweep_cases(), ids=lambda c: c.name)
 def test_length_sweep_sampled(case):
     x, got = run_case(case)
