@@ -481,10 +481,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   // when stored (see dkdv_f16_d128).
   float lsr = 0.f, dlr = 0.f;
   bool lrow = false;
-  auto issue_tile = [&](int t, T* base) {
+  const unsigned lds0 = lds_addr(smem);
+  const int qsb = (int)(a.q.ss * (int64_t)sizeof(T)), dsb = (int)(a.dout.ss * (int64_t)sizeof(T));
+  const int qlo = dma_lane_off<NW>(qsb), dlo = dma_lane_off<NW>(dsb);
+  auto issue_tile = [&](int t, int buf) {
     const int q0 = qstart + t * BM;
-    tile_dma<BM, NW>(rq, base, a.q.ss, q0);
-    tile_dma<BM, NW>(rd, base + TR, a.dout.ss, q0);
+    const unsigned base = lds0 + (unsigned)(buf * BUF * (int)sizeof(T));
+    tile_dma<BM, NW>(rq, base, qlo, qsb, q0);
+    tile_dma<BM, NW>(rd, base + (unsigned)(TR * (int)sizeof(T)), dlo, dsb, q0);
     const int i = q0 + ((int)threadIdx.x & (BM - 1));
     lrow = i < a.Sq;
     lsr = lse[min(i, a.Sq - 1)];
@@ -512,11 +516,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) qtp[tt][db] = sf0;
   if (ntiles > 0) {
-    issue_tile(0, smem);
+    issue_tile(0, 0);
     store_rows(0);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS
     __syncthreads();
-    if (ntiles > 1) issue_tile(1, smem + BUF);
+    if (ntiles > 1) issue_tile(1, 1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(smem, 0, ks * 2);
 #pragma unroll
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
         store_rows(t + 1);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile's buffer loads are in LDS
         __syncthreads();
-        if (t + 2 < ntiles) issue_tile(t + 2, cur);
+        if (t + 2 < ntiles) issue_tile(t + 2, t & 1);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(nq, nr, ks * 2);
       }
@@ -787,10 +791,13 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
 
   const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
   const int ntiles = (kend + BN - 1) / BN;
+  const unsigned lds0 = lds_addr(smem);
+  const int ksb = (int)(a.k.ss * (int64_t)sizeof(T)), vsb = (int)(a.v.ss * (int64_t)sizeof(T));
+  const int klo = dma_lane_off<NW>(ksb), vlo = dma_lane_off<NW>(vsb);
   auto issue_tile = [&](int t) {
-    T* base = smem + (t & 1) * BUF;
-    tile_dma<BN, NW>(rk, base, a.k.ss, t * BN);
-    tile_dma<BN, NW>(rv, base + TR, a.v.ss, t * BN);
+    const unsigned base = lds0 + (unsigned)((t & 1) * BUF * (int)sizeof(T));
+    tile_dma<BN, NW>(rk, base, klo, ksb, t * BN);
+    tile_dma<BN, NW>(rv, base + (unsigned)(TR * (int)sizeof(T)), vlo, vsb, t * BN);
   };
   if (ntiles > 0) issue_tile(0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS

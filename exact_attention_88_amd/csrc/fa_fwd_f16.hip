@@ -568,8 +568,15 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
   // addresses are a per-lane base plus constant offsets.
   auto kbuf = [&](int par) { return smem + (par & 1) * TR; };
   auto vbuf = [&](int par) { return smem + 2 * TR + (par & 1) * TR; };
-  auto dma_k = [&](int t, int par) { swzl::tile_dma<BN, NW>(rk, kbuf(par), a.k.ss, t * BN); };
-  auto dma_v = [&](int t, int par) { swzl::tile_dma<BN, NW>(rv, vbuf(par), a.v.ss, t * BN); };
+  const unsigned lds0 = swzl::lds_addr(smem);
+  const int ksb = (int)(a.k.ss * (int64_t)sizeof(T)), vsb = (int)(a.v.ss * (int64_t)sizeof(T));
+  const int klo = swzl::dma_lane_off<NW>(ksb), vlo = swzl::dma_lane_off<NW>(vsb);
+  auto dma_k = [&](int t, int par) {
+    swzl::tile_dma<BN, NW>(rk, lds0 + (unsigned)((par & 1) * TR * (int)sizeof(T)), klo, ksb, t * BN);
+  };
+  auto dma_v = [&](int t, int par) {
+    swzl::tile_dma<BN, NW>(rv, lds0 + (unsigned)((2 + (par & 1)) * TR * (int)sizeof(T)), vlo, vsb, t * BN);
+  };
   auto barrier = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS
     __syncthreads();

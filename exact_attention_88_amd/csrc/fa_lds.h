@@ -75,31 +75,49 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int nbytes) {
   return r;
 }
 
-// One wave-wide 16-byte-per-lane buffer load into LDS at lds (wave-uniform):
-// lane i's bytes land at lds + 16*i.  Issued as inline assembly so that the
-// compiler does not make every later LDS read wait for it: the caller waits
-// (vmcnt(0)) before the barrier that publishes the data.
-__device__ __forceinline__ void dma16(rsrc_t r, const void* lds, int voff) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)(__attribute__((address_space(3))) const void*)lds);
+// LDS byte address of a pointer into a __shared__ array (the m0 operand of
+// buffer loads into LDS).
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// One wave-wide 16-byte-per-lane buffer load into LDS at byte address m0
+// (wave-uniform): lane i's bytes land at m0 + 16*i.  Issued as inline
+// assembly so that the compiler does not make every later LDS read wait for
+// it: the caller waits (vmcnt(0)) before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(rsrc_t r, unsigned m0, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
 }
 
-// ROWS rows x 256 bytes into the swizzled layout at lds: ROWS/4 wave-wide
-// 1 KB loads (4 rows each) shared by the NW waves.
-template <int ROWS, int NW, class T>
-__device__ __forceinline__ void tile_dma(rsrc_t r, T* lds, int64_t ss, int row0) {
-  static_assert(ROWS % (4 * NW) == 0, "whole wave loads per wave");
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Rows of 16-bit elements, 256 bytes each, in LDS.
+constexpr int kRowBytes = kD * 2;
+
+// tile_dma moves ROWS rows x 256 bytes into the swizzled layout with
+// ROWS/(4*NW) wave-wide 1 KB loads (4 rows each) shared by the NW waves: load
+// i of wave w covers tile rows (i*NW + w)*4 .. +3, lane l row (i*NW + w)*4 +
+// l/16, its 16-byte chunk l%16 placed at chunk position (l%16) ^ swz(row).
+// With NW a multiple of 4 every load moves the rows by a multiple of 16,
+// which leaves swz(row) unchanged, so a lane's global byte offset is a
+// per-lane part fixed for the kernel (dma_lane_off, for row stride ss_bytes)
+// plus a wave-uniform row offset: one vector add per load.
+template <int NW>
+__device__ __forceinline__ int dma_lane_off(int ss_bytes) {
+  static_assert(NW % 4 == 0, "loads move whole multiples of 16 rows");
+  const int lane = threadIdx.x & 63, row = ((int)threadIdx.x >> 6) * 4 + (lane >> 4);
+  return row * ss_bytes + (((lane & 15) ^ swz(row)) << 4);
+}
+
+// ROWS rows starting at global row row0 into the tile at LDS byte address lds
+// (wave-uniform).  The caller guarantees that every byte offset fits in 31
+// bits; rows past the buffer's byte range read as zero.
+template <int ROWS, int NW>
+__device__ __forceinline__ void tile_dma(rsrc_t r, unsigned lds, int lane_off, int ss_bytes, int row0) {
+  static_assert(ROWS % (4 * NW) == 0 && NW % 4 == 0, "whole wave loads of 16-row multiples");
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 #pragma unroll
-  for (int i = 0; i < ROWS / (4 * NW); ++i) {
-    const int r0 = (i * NW + w) * 4;
-    const int row = r0 + (lane >> 4);
-    const int chunk = (lane & 15) ^ swz(row);
-    const int off = (int)((int64_t)(row0 + row) * ss * (int64_t)sizeof(T)) + chunk * 16;
-    dma16(r, lds + r0 * kD, off);
-  }
+  for (int i = 0; i < ROWS / (4 * NW); ++i)
+    dma16(r, lds + (unsigned)((i * NW + w) * 4 * kRowBytes), lane_off + (row0 + i * NW * 4) * ss_bytes);
 }
 
 }  // namespace swzl
