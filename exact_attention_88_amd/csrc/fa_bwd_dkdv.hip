@@ -52,13 +52,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     const T* orow = obase + (int64_t)i * a.o.ss;
     const T* drow = dbase + (int64_t)i * a.dout.ss;
     if (a.vec & VEC_O) {
-      __builtin_memcpy(ov[p], orow + col, 16);
+      const uint4 x = *reinterpret_cast<const uint4*>(orow + col);  // 16-byte aligned (checked on the host)
+      __builtin_memcpy(ov[p], &x, 16);
     } else {
 #pragma unroll
       for (int e = 0; e < CH; ++e) ov[p][e] = orow[(int64_t)(col + e) * a.o.sd];
     }
     if (a.vec & VEC_DO) {
-      __builtin_memcpy(dv[p], drow + col, 16);
+      const uint4 x = *reinterpret_cast<const uint4*>(drow + col);  // 16-byte aligned (checked on the host)
+      __builtin_memcpy(dv[p], &x, 16);
     } else {
 #pragma unroll
       for (int e = 0; e < CH; ++e) dv[p][e] = drow[(int64_t)(col + e) * a.dout.sd];
