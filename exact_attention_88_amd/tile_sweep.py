@@ -17,7 +17,10 @@ Workload per bucket S: B = max(1, 16384 // S) sequences of S tokens, H = 16
 heads (16k tokens per call, the shape of the length-sweep benchmark),
 Sq = Sk = S, contiguous [B, H, S, D], N(0, 1) inputs.  Each configuration is
 timed with HIP events over several interleaved rounds after a clock warm-up;
-the median per-call time decides.  Needs a GPU and the built library.
+the median per-call time decides.  A dQ configuration is timed together with
+the rowsum(dO.O) preprocess it needs: its own kernel, unless that
+configuration forms the rowsum inside the dQ kernel.  Needs a GPU and the
+built library.
 """
 from __future__ import annotations
 
@@ -67,7 +70,8 @@ def _time(torch, fns, rounds, min_ms):
     return [sorted(t)[len(t) // 2] for t in times]
 
 
-def sweep(torch, fa, rounds=3, min_ms=2.0, dtypes=None, dims=None, buckets=None, log=print):
+def sweep(torch, fa, rounds=3, min_ms=2.0, dtypes=None, dims=None, buckets=None, passes=None,
+          log=print):
     """{(pass, dtype code, D, causal, bucket): [ms per tile id]}."""
     res = {}
     seed = 0
@@ -94,10 +98,17 @@ def sweep(torch, fa, rounds=3, min_ms=2.0, dtypes=None, dims=None, buckets=None,
                         "fwd": lambda t: (lambda: fa.fa_fwd_tile(t, q, k, v, causal, out=oo, lse=ll)),
                         "dkdv": lambda t: (lambda: fa.fa_bwd_stage(1, t, q, k, v, o, do, lse, causal,
                                                                     dq=dq, dk=dk, dv=dv, delta=delta)),
-                        "dq": lambda t: (lambda: fa.fa_bwd_stage(2, t, q, k, v, o, do, lse, causal,
-                                                                  dq=dq, dk=dk, dv=dv, delta=delta)),
+                        # Stage 0 with dQ tile t launches the rowsum kernel only where
+                        # that tile does not form the rowsum itself.
+                        "dq": lambda t: (lambda: (
+                            fa.fa_bwd_stage(0, t, q, k, v, o, do, lse, causal,
+                                            dq=dq, dk=dk, dv=dv, delta=delta),
+                            fa.fa_bwd_stage(2, t, q, k, v, o, do, lse, causal,
+                                            dq=dq, dk=dk, dv=dv, delta=delta))),
                     }
                     for pi, p in enumerate(PASSES):
+                        if passes and p not in passes:
+                            continue
                         n = fa.fa_tile_count(pi, code, D)
                         ms = _time(torch, [fns[p](t) for t in range(n)], rounds, min_ms)
                         res[(p, code, D, causal, S)] = ms
@@ -152,6 +163,7 @@ def main(argv=None):
     ap.add_argument("--dtypes", default="", help="comma list of f16,f32,bf16 (default all)")
     ap.add_argument("--dims", default="", help="comma list of head dims (default all)")
     ap.add_argument("--buckets", default="", help="comma list of lengths (default 128..16384)")
+    ap.add_argument("--passes", default="", help="comma list of fwd,dkdv,dq (default all)")
     ap.add_argument("--merge", nargs="+", default=[],
                     help="no GPU: write --out from the --json files of earlier runs (later files win)")
     ap.add_argument("--device", default="", help="with --merge: the device the runs were made on")
@@ -178,7 +190,7 @@ def main(argv=None):
     del x
     lst = lambda s, f=str: [f(v) for v in s.split(",") if v]
     res = sweep(torch, fa, a.rounds, a.min_ms, lst(a.dtypes), lst(a.dims, int), lst(a.buckets, int),
-                log=lambda m: print(m, flush=True))
+                lst(a.passes), log=lambda m: print(m, flush=True))
     props = torch.cuda.get_device_properties(0)
     write_table(res, a.out, f"{props.gcnArchName.split(':')[0]} ({torch.cuda.get_device_name(0)})")
     if a.json:
