@@ -175,6 +175,63 @@ def test_contiguous_outputs_from_strided_inputs():
     check_full(case, x, got)
 
 
+def _in_layout(a, layout, tdt):
+    """Device copy of a logical [B,H,S,D] host array stored as ``layout``:
+    "bhsd" contiguous, "bshd" a transposed view (row stride H*D), "pad" rows
+    of D + 64 elements of which the first D are used."""
+    B, H, S, D = a.shape
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(tdt).cuda()
+    if layout == "bhsd":
+        return t
+    if layout == "bshd":
+        store = torch.empty((B, S, H, D), dtype=tdt, device="cuda").transpose(1, 2)
+    else:
+        store = torch.empty((B, H, S, D + 64), dtype=tdt, device="cuda")[..., :D]
+    store.copy_(t)
+    return store
+
+
+MIXED = [
+    W.Case("mixed_layouts_f16_causal", 2, 3, 777, 777, 128, "f16", 1, seed=811),
+    W.Case("mixed_layouts_f16", 2, 3, 777, 777, 128, "f16", 0, seed=812),
+    W.Case("mixed_layouts_bf16_causal", 2, 3, 777, 777, 128, "bf16", 1, seed=813),
+    W.Case("mixed_layouts_f16_bottom_right", 2, 3, 333, 901, 128, "f16", 2, seed=814),
+]
+
+
+@pytest.mark.parametrize("case", MIXED, ids=lambda c: c.name)
+def test_buffer_load_kernels_with_a_layout_per_operand(case):
+    """The buffer-load kernels (forward tile 4, dK/dV tile 4, dQ tile 5 of the
+    16-bit D = 128 lists) compute each operand's per-lane byte offsets from
+    that operand's own row stride: here Q is contiguous, K and dO are
+    transposed views, V and O have padded rows, dK and dV are transposed
+    views; ragged lengths (777 = 3*256 + 9 = 6*128 + 9) and, in one case,
+    Sq != Sk with bottom-right masking."""
+    fa = _fa()
+    x = W.make_inputs(case)
+    tdt = U.torch_dtype(case.dtype)
+    lay = dict(q="bhsd", k="bshd", v="pad", do="bshd")
+    dev = {n: _in_layout(a, lay[n], tdt) for n, a in x.items()}
+    B, H, Sq, Sk, D = case.B, case.H, case.Sq, case.Sk, case.D
+    o = _in_layout(np.full((B, H, Sq, D), np.nan, np.float32), "pad", tdt)
+    lse = U.nan_vec((B, H, Sq))
+    assert dev["k"].stride(2) != dev["v"].stride(2) != dev["q"].stride(2)
+    assert o.stride(2) != dev["do"].stride(2)
+    print(f"[gpu] fwd {case.name}", flush=True)
+    fa.fa_fwd_tile(4, dev["q"], dev["k"], dev["v"], case.causal, case.scale, out=o, lse=lse)
+    dq = U.empty_like_layout((B, H, Sq, D), tdt, "bhsd")
+    dk = U.empty_like_layout((B, H, Sk, D), tdt, "bshd")
+    dv = U.empty_like_layout((B, H, Sk, D), tdt, "bshd")
+    delta = U.nan_vec((B, H, Sq))
+    print(f"[gpu] bwd {case.name}", flush=True)
+    fa.fa_bwd_tile(4, 5, dev["q"], dev["k"], dev["v"], o, dev["do"], lse, case.causal,
+                   case.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+    torch.cuda.synchronize()
+    got = {n: U.host(t) for n, t in dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv,
+                                          delta=delta).items()}
+    check_full(case, x, got)
+
+
 def test_no_queries_gives_zero_key_gradients():
     fa = _fa()
     k = torch.randn(1, 2, 40, 64, device="cuda", dtype=torch.float16)
