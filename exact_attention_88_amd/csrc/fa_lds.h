@@ -95,8 +95,9 @@ constexpr int kRowBytes = kD * 2;
 
 // tile_dma moves ROWS rows x 256 bytes into the swizzled layout with
 // ROWS/(4*NW) wave-wide 1 KB loads (4 rows each) shared by the NW waves: load
-// i of wave w covers tile rows (i*NW + w)*4 .. +3, lane l row (i*NW + w)*4 +
-// l/16, its 16-byte chunk l%16 placed at chunk position (l%16) ^ swz(row).
+// i of wave w covers tile rows (i*NW + w)*4 .. +3; lane l takes row
+// (i*NW + w)*4 + l/16, fetches that row's 16-byte chunk (l%16) ^ swz(row) and
+// writes it at chunk position l%16 (so chunk k sits at position k ^ swz(row)).
 // With NW a multiple of 4 every load moves the rows by a multiple of 16,
 // which leaves swz(row) unchanged, so a lane's global byte offset is a
 // per-lane part fixed for the kernel (dma_lane_off, for row stride ss_bytes)
