@@ -48,3 +48,59 @@ def test_committed_table_is_complete():
     """Every cell of the compiled-in table was measured."""
     t = _swept_table()
     assert all(x >= 0 for p in t for d in p for h in d for c in h for x in c)
+
+
+def test_dq_entries_are_timed_with_the_rowsum_stage_they_need():
+    """The sweep times dQ entry t as stage 0 then stage 2 with the same tile
+    (stage 0 launches the rowsum kernel only where tile t does not form the
+    rowsum itself), and --passes restricts the passes swept.  Run on the CPU
+    with stand-ins for the GPU calls that record them."""
+    import types
+
+    import torch
+
+    calls = []
+
+    class Event:
+        def __init__(self, enable_timing=False):
+            pass
+
+        def record(self):
+            pass
+
+        def synchronize(self):
+            pass
+
+        def elapsed_time(self, other):
+            return 1.0
+
+    fake_torch = types.SimpleNamespace(
+        Generator=lambda device=None: torch.Generator(),
+        randn=lambda shape, generator=None, device=None, dtype=None: torch.randn(
+            shape, generator=generator, dtype=dtype),
+        empty_like=torch.empty_like, float16=torch.float16, float32=torch.float32,
+        bfloat16=torch.bfloat16,
+        cuda=types.SimpleNamespace(Event=Event, synchronize=lambda: None,
+                                   empty_cache=lambda: None))
+
+    class FA:
+        def fa_fwd(self, q, k, v, causal):
+            return torch.empty_like(q), torch.empty(q.shape[:3])
+
+        def fa_tile_count(self, p, code, D):
+            return 3
+
+        def fa_fwd_tile(self, t, *a, **k):
+            calls.append(("fwd", t))
+
+        def fa_bwd_stage(self, stage, t, *a, **k):
+            calls.append((stage, t))
+
+    res = TS.sweep(fake_torch, FA(), rounds=1, min_ms=0.0, dtypes=["f16"], dims=[16],
+                   buckets=[128], passes=["dq"], log=lambda m: None)
+    assert sorted(res) == [("dq", 0, 16, c, 128) for c in (0, 1)]
+    timed = [c for c in calls if c != (0, -1)]  # (0, -1): the delta set-up per causal flag
+    assert timed and all(c[0] != "fwd" and c[0] != 1 for c in timed)
+    assert len(timed) % 2 == 0
+    for a, b in zip(timed[::2], timed[1::2]):
+        assert a[0] == 0 and b[0] == 2 and a[1] == b[1], (a, b)
