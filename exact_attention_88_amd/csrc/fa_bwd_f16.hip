@@ -36,12 +36,6 @@ using namespace swzl;
 constexpr int kLSR = kD + 8;   // row-read layout stride (halfs): 272 bytes
 constexpr int kLST = kD + 32;  // transposed-read layout stride (halfs): 320 bytes
 
-__device__ __forceinline__ int xcd_logical_block() {
-  const int n = gridDim.x, id = blockIdx.x;
-  if (n % 8 != 0) return id;
-  return (id % 8) * (n / 8) + id / 8;
-}
-
 template <int ROWS, int NT, class T>
 __device__ __forceinline__ void tile_load(u32x4* r, const T* __restrict__ base, int64_t ss,
                                           int row0, int nrows) {
@@ -123,9 +117,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_f16_d128(BwdArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nqb = (a.Sq + BM - 1) / BM;
-  const int L = xcd_logical_block();
-  int qb = L % nqb;
-  const int bh = L / nqb;
+  int qb, bh;
+  xcd_block(nqb, CAUSAL, qb, bh);
   if (CAUSAL) qb = nqb - 1 - qb;
   const int b = bh / a.H, h = bh % a.H;
   const T* kbase = (const T*)a.k.p + b * a.k.sb + h * a.k.sh;
@@ -248,9 +241,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nkb = (a.Sk + BN - 1) / BN;
-  const int L = xcd_logical_block();
-  const int kb = L % nkb;  // causal: lowest key blocks (most work) first
-  const int bh = L / nkb;
+  int kb, bh;  // causal: lowest key blocks (most work) first
+  xcd_block(nkb, false, kb, bh);
   const int b = bh / a.H, h = bh % a.H;
   const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
   const T* dobase = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh;
@@ -437,9 +429,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nkb = (a.Sk + BN - 1) / BN;
-  const int L = xcd_logical_block();
-  const int kb = L % nkb;
-  const int bh = L / nkb;
+  int kb, bh;
+  xcd_block(nkb, false, kb, bh);
   const int b = bh / a.H, h = bh % a.H;
   const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
   const T* dobase = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh;
@@ -733,9 +724,8 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
   const int lane = threadIdx.x & 63, g = lane >> 5, c = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int nqb = (a.Sq + BM - 1) / BM;
-  const int L = xcd_logical_block();
-  int qb = L % nqb;
-  const int bh = L / nqb;
+  int qb, bh;
+  xcd_block(nqb, CAUSAL, qb, bh);
   if (CAUSAL) qb = nqb - 1 - qb;
   const int b = bh / a.H, h = bh % a.H;
   const T* kbase = (const T*)a.k.p + b * a.k.sb + h * a.k.sh;

@@ -37,14 +37,6 @@ constexpr int kD = 128;
 constexpr int kLSK = kD + 8;   // K tile row stride (halfs): 272 bytes
 constexpr int kLSV = kD + 32;  // V tile row stride (halfs): 320 bytes
 
-// Map the hardware workgroup id to (query block, batch*head) so that
-// consecutive logical blocks share an XCD.
-__device__ __forceinline__ int xcd_logical_block() {
-  const int n = gridDim.x, id = blockIdx.x;
-  if (n % 8 != 0) return id;
-  return (id % 8) * (n / 8) + id / 8;
-}
-
 // Global -> register staging of a ROWS x 128 fp16 tile (16-byte chunks,
 // PER per thread) and register -> padded LDS store.  Native vector types keep
 // the staging in VGPRs.
@@ -105,9 +97,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128(FwdArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nqb = (a.Sq + BM - 1) / BM;
-  const int L = xcd_logical_block();
-  int qb = L % nqb;
-  const int bh = L / nqb;
+  int qb, bh;
+  xcd_block(nqb, CAUSAL, qb, bh);
   if (CAUSAL) qb = nqb - 1 - qb;
   const int b = bh / a.H, h = bh % a.H;
   const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
@@ -346,9 +337,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nqb = (a.Sq + BM - 1) / BM;
-  const int L = xcd_logical_block();
-  int qb = L % nqb;
-  const int bh = L / nqb;
+  int qb, bh;
+  xcd_block(nqb, CAUSAL, qb, bh);
   if (CAUSAL) qb = nqb - 1 - qb;
   const int b = bh / a.H, h = bh % a.H;
   const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
@@ -528,9 +518,8 @@ __global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nqb = (a.Sq + BM - 1) / BM;
-  const int L = xcd_logical_block();
-  int qb = L % nqb;
-  const int bh = L / nqb;
+  int qb, bh;
+  xcd_block(nqb, CAUSAL, qb, bh);
   if (CAUSAL) qb = nqb - 1 - qb;
   const int b = bh / a.H, h = bh % a.H;
   const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;

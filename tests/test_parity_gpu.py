@@ -232,6 +232,22 @@ def test_buffer_load_kernels_with_a_layout_per_operand(case):
     check_full(case, x, got)
 
 
+MANY_HEADS = [
+    W.Case("many_heads_f16_causal", 8, 8, 300, 300, 128, "f16", 1, seed=821),
+    W.Case("many_heads_bf16_causal", 4, 16, 300, 300, 128, "bf16", 1, seed=822),
+    W.Case("many_heads_f16_bottom_right", 8, 8, 200, 300, 128, "f16", 2, seed=823),
+]
+
+
+@pytest.mark.parametrize("case", MANY_HEADS, ids=lambda c: c.name)
+def test_causal_block_order_across_heads(case):
+    """64 (b,h) pairs: every XCD holds 8 whole heads, so the causal kernels
+    hand out their blocks rank by rank across those heads (largest first);
+    every output element is still written once and matches the oracle."""
+    x, got = run_case(case)
+    check_full(case, x, got)
+
+
 def test_no_queries_gives_zero_key_gradients():
     fa = _fa()
     k = torch.randn(1, 2, 40, 64, device="cuda", dtype=torch.float16)
