@@ -67,12 +67,11 @@ template <> struct Mfma<float> {
 
 // Workgroup -> (block rank within its (b,h), b*h).  Workgroups go out to the
 // 8 XCDs round robin (id % 8); each (b,h)'s nb blocks stay on one XCD so that
-// its L2 serves their shared K/V (or Q/dO) stream.  With by_rank and at least
-// 8 whole heads per XCD, an XCD's workgroups go out rank by rank across its
+// its L2 serves their shared K/V (or Q/dO) stream.  With by_rank, and whole
+// heads on every XCD, an XCD's workgroups go out rank by rank across its
 // heads (rank 0 of every head first) rather than head by head: the causal
 // kernels give rank 0 the most work, so this is longest-first scheduling and
-// the launch does not end on a few long blocks of the last heads.  With
-// fewer heads per XCD each head's blocks already fill most of it.  (The
+// the launch does not end on the long blocks of the XCD's last head.  (The
 // forward and dQ kernels take it; dK/dV, whose key blocks share one Q/dO
 // stream per head, measured slightly slower with it.)
 __device__ __forceinline__ void xcd_block(int nb, bool by_rank, int& rank, int& bh) {
@@ -80,7 +79,7 @@ __device__ __forceinline__ void xcd_block(int nb, bool by_rank, int& rank, int& 
   int L = id;
   if (n % 8 == 0) {
     const int per = n / 8, x = id % 8, slot = id / 8;
-    if (by_rank && per % nb == 0 && per / nb >= 8) {
+    if (by_rank && per % nb == 0) {
       const int hx = per / nb;
       rank = slot / hx;
       bh = x * hx + slot % hx;
