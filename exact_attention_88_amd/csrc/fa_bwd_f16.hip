@@ -242,7 +242,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nkb = (a.Sk + BN - 1) / BN;
   int kb, bh;  // causal: lowest key blocks (most work) first
-  xcd_block(nkb, false, kb, bh);
+  xcd_block(nkb, CAUSAL, kb, bh);
   const int b = bh / a.H, h = bh % a.H;
   const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
   const T* dobase = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh;
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nkb = (a.Sk + BN - 1) / BN;
   int kb, bh;
-  xcd_block(nkb, false, kb, bh);
+  xcd_block(nkb, CAUSAL, kb, bh);
   const int b = bh / a.H, h = bh % a.H;
   const T* qbase = (const T*)a.q.p + b * a.q.sb + h * a.q.sh;
   const T* dobase = (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh;

@@ -71,9 +71,8 @@ template <> struct Mfma<float> {
 // heads on every XCD, an XCD's workgroups go out rank by rank across its
 // heads (rank 0 of every head first) rather than head by head: the causal
 // kernels give rank 0 the most work, so this is longest-first scheduling and
-// the launch does not end on the long blocks of the XCD's last head.  (The
-// forward and dQ kernels take it; dK/dV, whose key blocks share one Q/dO
-// stream per head, measured slightly slower with it.)
+// the launch does not end on the long blocks of the XCD's last head.  The
+// causal forward, dQ and dK/dV kernels take it.
 __device__ __forceinline__ void xcd_block(int nb, bool by_rank, int& rank, int& bh) {
   const int n = gridDim.x, id = blockIdx.x;
   int L = id;
