@@ -3,6 +3,7 @@
 // launches on the caller's stream.
 #include "../../include/fa.h"
 
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 
@@ -40,6 +41,10 @@ bool vec_ok(const void* p, const int64_t* s, int es) {
   return s[3] == 1 && (a % 16) == 0 && (s[0] * es) % 16 == 0 && (s[1] * es) % 16 == 0 &&
          (s[2] * es) % 16 == 0;
 }
+
+// The kernels need scale * log2(e) > 0: the running max only rises, and
+// masked scores are -inf (0 * -inf would be NaN).
+bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
 
 T4 mk(const void* p, const int64_t* s) { return T4{p, s[0], s[1], s[2], s[3]}; }
 
@@ -82,6 +87,7 @@ int fwd_impl(int tile, const void* q, const int64_t* qs, const void* k, const in
   int st = shape_check(B, H, Sq, Sk, D, dtype);
   if (st != FA_OK) return st;
   if (causal < 0 || causal > 2) return FA_ERR_CAUSAL;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
   if (B * H * Sq == 0) return FA_OK;
   if (!q || !k || !v || !out || !lse) return FA_ERR_NULL;
   if (!qs || !ks || !vs || !os) return FA_ERR_NULL;
@@ -123,6 +129,7 @@ int bwd_impl(int stage, int tile_kv, int tile_q, const void* q, const int64_t* q
   int st = shape_check(B, H, Sq, Sk, D, dtype);
   if (st != FA_OK) return st;
   if (causal < 0 || causal > 2) return FA_ERR_CAUSAL;
+  if (!scale_ok(scale)) return FA_ERR_SCALE;
   if (B * H == 0 || (Sq == 0 && Sk == 0)) return FA_OK;
   const bool has_q = Sq > 0;
   if (!k || !v || !dk || !dv || !ks || !vs || !dks || !dvs) return FA_ERR_NULL;
@@ -303,13 +310,19 @@ const char* fa_status_string(int status) {
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error at launch";
     case FA_ERR_TILE: return "FA_ERR_TILE: tile id out of range";
     case FA_ERR_CAUSAL: return "FA_ERR_CAUSAL: causal must be 0, 1 (top-left) or 2 (bottom-right)";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
   }
   return "unknown fa_status";
 }
 
 const char* fa_last_hip_error(void) { return g_last_hip; }
 
-const char* fa_version(void) { return "fa-mi355x 0.1 gfx950"; }
+#define FA_STR2(x) #x
+#define FA_STR(x) FA_STR2(x)
+const char* fa_version(void) {
+  return "fa-mi355x 0.2 gfx950; HIP " FA_STR(HIP_VERSION_MAJOR) "." FA_STR(HIP_VERSION_MINOR) "." FA_STR(
+      HIP_VERSION_PATCH) "; " __VERSION__;
+}
 
 int64_t fa_probe_threads(void) { return (int64_t)fa::probe_workgroups() * 256; }
 

@@ -1,10 +1,12 @@
 // Backward dK/dV kernel for gfx950, and the rowsum(dO.O) preprocess.
 //
-// Method ("Triton FlashAttention": the backward split the FlashAttention-2
-// way into a dK/dV kernel and a dQ kernel with no atomics, probabilities
-// rebuilt from the saved log-sum-exp, rowsum(dO.O) in its own small kernel;
-// "FlashAttention-2 from PyTorch to Triton", the backward outline: L, the
-// precomputed D = rowsum(dO o O) and a loop over query tiles per key tile).
+// Method: "Triton FlashAttention", opening summary (a backward with no
+// atomics: key-side gradients and query-side gradients are produced by two
+// separate kernels, each recomputing the probabilities from the forward's
+// saved log-sum-exp, after a small kernel that forms the per-row dot product
+// of dO with O); "FlashAttention-2 from PyTorch to Triton", backward outline
+// (each key tile visits every query tile, using L and that per-row dot
+// product).
 //
 // One workgroup owns BN = 32*waves keys of one (batch, head); each wave keeps
 // its 32 keys' K and V fragments in registers and accumulates dK^T and dV^T

@@ -1,9 +1,9 @@
 // Backward dQ kernel for gfx950.
 //
-// Method ("Triton FlashAttention": the dQ kernel of the FlashAttention-2
-// backward split, one program per query block looping over key blocks, so
-// that nothing needs atomics; probabilities rebuilt from the saved
-// log-sum-exp).
+// Method: "Triton FlashAttention", opening summary (the query-side half of
+// the atomic-free backward).  Each workgroup owns a block of query rows and
+// visits the key tiles it can see, so every dQ row has exactly one writer;
+// the probabilities are recomputed from the saved log-sum-exp.
 //
 // One workgroup owns BM = 32*waves query rows of one (batch, head); each wave
 // keeps its 32 rows' Q and dO fragments, LSE and delta in registers and

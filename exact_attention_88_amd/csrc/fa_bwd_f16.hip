@@ -1,11 +1,11 @@
 // Backward dK/dV and dQ kernels for 16-bit inputs (fp16, bf16) with head dim
 // 128 on gfx950: the tuned path.
 //
-// Same method as the generic backward kernels ("Triton FlashAttention": the
-// FlashAttention-2 split into a dK/dV kernel and a dQ kernel with no atomics,
-// probabilities rebuilt from the saved log-sum-exp; "FlashAttention-2 from
-// PyTorch to Triton", the backward outline), laid out for CDNA4 like the tuned
-// forward kernel:
+// Same method as the generic backward kernels ("Triton FlashAttention",
+// opening summary: key-side and query-side gradients from two kernels, no
+// atomics, probabilities recomputed from the saved log-sum-exp;
+// "FlashAttention-2 from PyTorch to Triton", backward outline), laid out for
+// CDNA4 like the tuned forward kernel:
 //   * the streamed tiles are double-buffered in LDS through registers (the
 //     global loads of tile t+1 are issued before tile t is computed), one
 //     barrier per tile;

@@ -199,6 +199,34 @@ def _causal_code(causal):
     return int(causal)
 
 
+def _check_layout(q, k, v, outs_like_q=(), outs_like_k=(), rows=()):
+    """Shapes and dtypes of every tensor against q's [B, H, Sq, D] and k's
+    Sk, before anything reaches the library: the C ABI takes one set of sizes
+    and one dtype for all tensors, so a short or differently typed tensor
+    would be read or written past its end by the kernels."""
+    for t in (q, k, v) + tuple(outs_like_q) + tuple(outs_like_k):
+        if t.dim() != 4:
+            raise ValueError("fa expects [B, H, S, D] tensors")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if tuple(k.shape) != (B, H, Sk, D) or tuple(v.shape) != (B, H, Sk, D):
+        raise ValueError(f"k and v must both be [B, H, Sk, D] = [{B}, {H}, {Sk}, {D}] "
+                         f"(got {tuple(k.shape)} and {tuple(v.shape)})")
+    for t in outs_like_q:
+        if tuple(t.shape) != (B, H, Sq, D):
+            raise ValueError(f"expected a [B, H, Sq, D] = {(B, H, Sq, D)} tensor, got {tuple(t.shape)}")
+    for t in outs_like_k:
+        if tuple(t.shape) != (B, H, Sk, D):
+            raise ValueError(f"expected a [B, H, Sk, D] = {(B, H, Sk, D)} tensor, got {tuple(t.shape)}")
+    for t in (k, v) + tuple(outs_like_q) + tuple(outs_like_k):
+        if t.dtype != q.dtype:
+            raise ValueError(f"every tensor must have q's dtype {q.dtype} (got {t.dtype})")
+    import torch
+    for t in rows:
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, Sq):
+            raise ValueError(f"lse and delta must be contiguous float32 [B, H, Sq] = {(B, H, Sq)}")
+
+
 def _check_same_device(ref, *ts):
     for t in ts:
         if not t.is_cuda or t.device != ref.device:
@@ -212,6 +240,8 @@ def fa_fwd_tile(tile_id, q, k, v, causal=False, scale=None, out=None, lse=None):
     float32 ``[B, H, Sq]`` (natural log).
     """
     import torch
+    _check_layout(q, k, v, (out,) if out is not None else (), (),
+                  (lse,) if lse is not None else ())
     _check_4d(q, k, v)
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
@@ -221,8 +251,6 @@ def fa_fwd_tile(tile_id, q, k, v, causal=False, scale=None, out=None, lse=None):
         out = torch.empty((B, H, Sq, D), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    if lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, Sq]")
     _check_4d(q, k, v, out)
     _check_same_device(q, lse)
     st = _lib.fa_fwd_tile(int(tile_id), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
@@ -244,6 +272,9 @@ def fa_bwd_tile(dkdv_tile, dq_tile, q, k, v, o, dout, lse, causal=False, scale=N
     Returns ``(dq, dk, dv, delta)``.
     """
     import torch
+    _check_layout(q, k, v, tuple(t for t in (o, dout, dq) if t is not None),
+                  tuple(t for t in (dk, dv) if t is not None),
+                  tuple(t for t in (lse, delta) if t is not None))
     _check_4d(q, k, v, o, dout)
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
@@ -257,9 +288,6 @@ def fa_bwd_tile(dkdv_tile, dq_tile, q, k, v, o, dout, lse, causal=False, scale=N
         dv = torch.empty((B, H, Sk, D), dtype=v.dtype, device=v.device)
     if delta is None:
         delta = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    for t in (lse, delta):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("lse and delta must be contiguous float32 [B, H, Sq]")
     _check_4d(q, k, v, o, dout, dq, dk, dv)
     _check_same_device(q, lse, delta)
     args = (_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(o),

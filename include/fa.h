@@ -72,7 +72,11 @@ typedef enum {
   FA_ERR_ALIAS = -5,  /* an output base pointer equals an input's or another output's */
   FA_ERR_HIP = -6,    /* the HIP runtime reported an error at launch */
   FA_ERR_TILE = -7,   /* a forced tile id is out of range for this pass, dtype and D */
-  FA_ERR_CAUSAL = -8  /* causal is not 0, 1 or 2 */
+  FA_ERR_CAUSAL = -8, /* causal is not 0, 1 or 2 */
+  FA_ERR_SCALE = -9   /* scale is not a finite number > 0 (the kernels take the softmax over
+                         scale * q.k in base 2 with the running max raised, never lowered, which
+                         needs a positive scale; masked scores are -inf, so scale = 0 would give
+                         0 * inf) */
 } fa_status;
 
 /* Pass ids for the tile-table queries. */
@@ -89,7 +93,8 @@ typedef enum { FA_PASS_FWD = 0, FA_PASS_BWD_DKDV = 1, FA_PASS_BWD_DQ = 2 } fa_pa
  *
  * q: [B,H,Sq,D], k and v: [B,H,Sk,D], out: [B,H,Sq,D] (dtype), lse: [B,H,Sq]
  * contiguous float32.  `scale` is applied to the fp32 scores (typically
- * 1/sqrt(D)).  B*H*Sq == 0 is a successful no-op.
+ * 1/sqrt(D)); it must be finite and > 0 (else FA_ERR_SCALE).  B*H*Sq == 0 is a
+ * successful no-op.
  */
 int fa_fwd(const void* q, const int64_t q_strides[4],
            const void* k, const int64_t k_strides[4],
@@ -113,7 +118,8 @@ int fa_fwd(const void* q, const int64_t q_strides[4],
  * q, k, v, o (= fa_fwd's out), dO and lse (= fa_fwd's lse for the same
  * inputs) are read; delta_ws is a caller-owned float32 [B,H,Sq] workspace
  * that is overwritten (it holds delta afterwards); dq [B,H,Sq,D], dk and dv
- * [B,H,Sk,D] are overwritten.  The kernels run in order on `stream`: the
+ * [B,H,Sk,D] are overwritten.  `scale` must be the forward's (finite, > 0,
+ * else FA_ERR_SCALE).  The kernels run in order on `stream`: the
  * rowsum, the dQ kernel, the dK/dV kernel; where the dQ kernel can form delta
  * from the query rows it holds (16-bit, D = 128, 16-byte-aligned rows) there
  * is no separate rowsum launch and the dQ kernel writes delta_ws.
@@ -234,7 +240,9 @@ const char* fa_status_string(int status);
  * FA_ERR_HIP (hipGetErrorName: hipGetErrorString), or "" if none occurred. */
 const char* fa_last_hip_error(void);
 
-/* Library version string, e.g. "fa-mi355x 0.1 gfx950". */
+/* Library version string: name, version and target, then the HIP version and
+ * the compiler that built it, e.g. "fa-mi355x 0.2 gfx950; HIP 7.2.x; AMD
+ * clang version ...". */
 const char* fa_version(void);
 
 #ifdef __cplusplus

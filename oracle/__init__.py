@@ -7,7 +7,9 @@ path; the two meet only in the seeded input generators of
 ``exact_attention_88_amd.workloads``, which hold no attention arithmetic.
 """
 from .attention import (attention_forward, attention_backward, delta_rowsum, head_forward,
-                        head_backward, head_forward_rows, head_backward_rows, causal_offset)
+                        head_backward, head_forward_rows, head_backward_rows,
+                        head_backward_qrows, causal_offset)
 
 __all__ = ["attention_forward", "attention_backward", "delta_rowsum", "head_forward",
-           "head_backward", "head_forward_rows", "head_backward_rows", "causal_offset"]
+           "head_backward", "head_forward_rows", "head_backward_rows", "head_backward_qrows",
+           "causal_offset"]

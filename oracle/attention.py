@@ -51,7 +51,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["attention_forward", "attention_backward", "delta_rowsum", "head_forward",
-           "head_backward", "head_forward_rows", "head_backward_rows", "causal_offset"]
+           "head_backward", "head_forward_rows", "head_backward_rows", "head_backward_qrows",
+           "causal_offset"]
 
 ROW_BLOCK = 2048
 
@@ -209,3 +210,22 @@ def head_backward_rows(q, k, v, do, scale, causal, q_rows, k_rows, row_block=ROW
     ds = p * (do @ v[k_rows].T - psum[:, None])
     dk = scale * (ds.T @ q)
     return dq, dk, dv
+
+
+def head_backward_qrows(q, k, v, do, scale, causal, rows):
+    """dq at the given absolute query rows only.
+
+    A query row's gradient needs nothing beyond its own full score row: its
+    LSE, its probabilities and its softmax term sum_k P_ik dP_ik all come from
+    that row, so this is the definition of ``head_backward`` restricted to the
+    sampled rows (the key-side gradients, which need every row, are what
+    ``head_backward_rows`` is for).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    rows = np.asarray(rows, dtype=np.int64)
+    off = causal_offset(causal, q.shape[0], k.shape[0])
+    s = _mask(scale * (q[rows] @ k.T), rows, np.arange(k.shape[0]), off)
+    p = _probs(s, _lse(s))
+    dp = do[rows] @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return scale * (ds @ k)

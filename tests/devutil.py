@@ -6,10 +6,13 @@ are tighter):
   float32: max |x - ref| <= 2e-5 for O and LSE, <= 1e-4 for dQ, dK, dV;
   float16: max |x - ref| / max |ref| <= 2e-3 for O and <= 1e-2 for dQ, dK, dV,
            and max |lse - ref| <= 2e-3 (LSE is float32 from float32 sums);
-  bfloat16: the float16 bars scaled by the ratio of the unit roundoffs
-           (2^-8 against 2^-11: the errors come from rounding P, dS and the
-           outputs to the 16-bit type), 1.6e-2 for O and 8e-2 for the
-           gradients, relative to max |ref|; LSE as for float16.
+  bfloat16: 1.6e-2 for O (the float16 bar scaled by the ratio of the unit
+           roundoffs, 2^-8 against 2^-11: the errors come from rounding P and
+           the output to the 16-bit type) and 2e-2 for dQ, dK, dV, relative
+           to max |ref| (roughly the float16 gradient bar scaled the same way,
+           capped at the value the objective's bfloat16 row gives); LSE as
+           for float16.  Measured errors sit near 4e-3 (O) and at most about
+           1.1e-2 (gradients, peaked softmax).
 """
 from __future__ import annotations
 
@@ -18,7 +21,7 @@ import numpy as np
 TOL = {
     "f32": {"o": 2e-5, "lse": 2e-5, "grad": 1e-4},
     "f16": {"o": 2e-3, "lse": 2e-3, "grad": 1e-2},
-    "bf16": {"o": 1.6e-2, "lse": 2e-3, "grad": 8e-2},
+    "bf16": {"o": 1.6e-2, "lse": 2e-3, "grad": 2e-2},
 }
 
 
@@ -74,3 +77,9 @@ def err(x, ref, dtype, kind):
 
 def tol(dtype, kind):
     return TOL[dtype]["grad" if kind in ("dq", "dk", "dv") else kind]
+
+
+def delta_tol(dtype):
+    """Bar on delta = rowsum(dO o O) against the same sum over the device's own
+    O, relative to max(1, max |ref|): the device accumulates in fp32."""
+    return {"f32": 1e-5, "f16": 2e-3, "bf16": 1.6e-2}[dtype]

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert "gfx950" in fa.fa_version()
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         assert fa.fa_status_string(code).startswith("FA_")
     assert "unknown" in fa.fa_status_string(-99)
 

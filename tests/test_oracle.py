@@ -435,3 +435,16 @@ def test_sampled_rows_match_full_evaluation():
         assert np.max(np.abs(dq2 - dq[rows])) < 1e-12
         assert np.max(np.abs(dk2 - dk[krows])) < 1e-12
         assert np.max(np.abs(dv2 - dv[krows])) < 1e-12
+
+
+def test_query_rows_backward_matches_full_evaluation():
+    """dq of sampled query rows alone (no key-side work) equals whole-head
+    evaluation, top-left and bottom-right causal and not, Sq != Sk."""
+    rng = _rng(15)
+    for causal, Sq, Sk in ((False, 37, 29), (True, 37, 37), (2, 23, 41), (2, 41, 23)):
+        q, do = _rand(rng, Sq, 6), _rand(rng, Sq, 6)
+        k, v = _rand(rng, Sk, 6), _rand(rng, Sk, 6)
+        dq, _, _ = oracle.head_backward(q, k, v, do, 0.35, causal)
+        rows = [0, 3, Sq // 2, Sq - 1]
+        dq2 = oracle.head_backward_qrows(q, k, v, do, 0.35, causal, rows)
+        assert np.max(np.abs(dq2 - dq[rows])) < 1e-12
