@@ -73,6 +73,9 @@ def parse():
                     help="skip the secondary bfloat16 timing of the same workload")
     ap.add_argument("--no-flush", action="store_true",
                     help="time back-to-back steps without the cache flush (for comparison only)")
+    ap.add_argument("--seq", type=int, default=0,
+                    help="time the length-sweep workload at this S (fp16 causal, H=16, D=128, "
+                         "B=16384/S) in place of the long-context one (for per-length profiles)")
     return ap.parse_args()
 
 
@@ -141,9 +144,10 @@ def _pci_bus_id(torch):
 
 class Sensors:
     """Shader clock and board power of the benchmarked GPU from its sysfs node
-    (hwmon freq1_input in Hz, power1_average or power1_input in microwatts),
-    sampled by a background thread while a timed region runs.  Records what
-    the box exposes and says so when it exposes nothing."""
+    (hwmon freq1_input in Hz, or the DPM level marked current in pp_dpm_sclk;
+    hwmon power1_average or power1_input in microwatts), sampled by a
+    background thread while a timed region runs.  Records what the box
+    exposes and says so when it exposes nothing."""
 
     def __init__(self, pci):
         self.files = {}
@@ -189,13 +193,17 @@ class Sensors:
                 out[key] = int(txt.strip()) / 1e6
             elif key == "power_w":
                 out[key] = int(txt.strip()) / 1e6
-            else:
+            else:  # the DPM level marked current, e.g. "1: 1896Mhz *"
                 cur = [ln for ln in txt.splitlines() if ln.strip().endswith("*")]
                 if cur:
-                    out["dpm_sclk"] = cur[0].split(":")[1].strip(" *")
+                    val = cur[0].split(":")[1].strip(" *").lower().replace("mhz", "")
+                    try:
+                        out["dpm_sclk_mhz"] = float(val)
+                    except ValueError:
+                        pass
         return out
 
-    def start(self, period=0.02):
+    def start(self, period=0.005):
         self.samples = []
         if not self.files:
             return
@@ -218,14 +226,11 @@ class Sensors:
 
     def summary(self):
         rec = {"source": self.source, "samples": len(self.samples)}
-        for key in ("sclk_mhz", "power_w"):
+        for key in ("sclk_mhz", "dpm_sclk_mhz", "power_w"):
             vals = [s[key] for s in self.samples if key in s]
             if vals:
                 rec[key] = {"min": round(min(vals), 1), "median": round(statistics.median(vals), 1),
                             "max": round(max(vals), 1)}
-        dpm = [s["dpm_sclk"] for s in self.samples if "dpm_sclk" in s]
-        if dpm:
-            rec["dpm_sclk_last"] = dpm[-1]
         return rec
 
 
@@ -649,6 +654,8 @@ def main():
     smi_start = smi_snapshot()
     flush = Flusher(torch, enabled=not args.no_flush)
     case = W.long_case()
+    if args.seq:
+        case = next(c for c in W.sweep_cases() if c.Sq == args.seq and c.causal)
     x, dev = make_device_inputs(case, torch)
     r = time_path(fa, torch, case, dev, args.steps, args.warmup, flush, sensors)
     med, mean = r["median"], r["mean"]
@@ -681,7 +688,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic: Q,K,V,dO iid N(0,1) rounded to fp16, seed 4",
-        "config": {"workload": "long-context causal fp16 attention fwd+bwd, B=1 H=16 S=16384 D=128",
+        "config": {"workload": (f"{'long-context' if not args.seq else 'length-sweep'} causal fp16 "
+                                f"attention fwd+bwd, B={case.B} H={case.H} S={case.Sq} D={case.D}"),
                    "B": case.B, "H": case.H, "S": case.Sq, "D": case.D, "causal": True},
         "timing": {"statistic": "median of per-step HIP-event times",
                    "flush_before_each_step_bytes": 0 if args.no_flush else FLUSH_BYTES,
