@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "fa_args.h"
 
 namespace {
@@ -119,7 +121,8 @@ int fwd_impl(int tile, const void* q, const int64_t* qs, const void* k, const in
   return hip_status(fa::launch_fwd(a, dt, d, causal ? 1 : 0, tile, (hipStream_t)stream));
 }
 
-// stage: -1 = all three kernels; 0 = preprocess; 1 = dK/dV; 2 = dQ.
+// stage: -1 = all three kernels; 0 = preprocess; 1 = dK/dV; 2 = dQ;
+// -2 = validate the arguments and launch nothing.
 int bwd_impl(int stage, int tile_kv, int tile_q, const void* q, const int64_t* qs, const void* k,
              const int64_t* ks, const void* v, const int64_t* vs, const void* o,
              const int64_t* os, const void* dout, const int64_t* dos, const float* lse,
@@ -186,6 +189,7 @@ int bwd_impl(int stage, int tile_kv, int tile_q, const void* q, const int64_t* q
   // chosen dQ kernel can form it from the rows it holds, from the dQ kernel
   // (stage 2), which then runs first; the dK/dV kernel (stage 1) reads it.
   a.fuse_delta = has_q && fa::dq_can_fuse_delta(a, dt, d, tile_q) ? 1 : 0;
+  if (stage == -2) return FA_OK;  // validation only (fa_bwd_noalloc's pre-check)
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (has_q && !a.fuse_delta && (stage < 0 || stage == 0)) e = fa::launch_bwd_pre(a, dt, d, s);
@@ -196,9 +200,69 @@ int bwd_impl(int stage, int tile_kv, int tile_q, const void* q, const int64_t* q
   return hip_status(e);
 }
 
+// Scratch of the allocation-free backward (fa_bwd_noalloc): the delta
+// workspace, one array per device in the library's own device globals, so
+// the call allocates nothing.  Host code never passes `scratch` itself to a
+// kernel (in host code the name is a host-side stand-in, not the device
+// array): each device's address comes from hipGetSymbolAddress, taken once
+// per device on its first call with that device current.
+constexpr int64_t kScratchRows = (int64_t)1 << 22;  // delta floats: B*H*Sq limit, 16 MiB
+__device__ __attribute__((aligned(256))) float scratch[kScratchRows];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+
+// This device's scratch address (FA_OK) or a fa_status.
+int scratch_for_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return FA_ERR_HIP;
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_bwd_noalloc(const void* q, const int64_t q_strides[4], const void* k,
+                   const int64_t k_strides[4], const void* v, const int64_t v_strides[4],
+                   const void* o, const int64_t o_strides[4], const void* dout,
+                   const int64_t dout_strides[4], const float* lse, int64_t B, int64_t H,
+                   int64_t Sq, int64_t Sk, int64_t D, int causal, float scale, int dtype,
+                   void* dq, const int64_t dq_strides[4], void* dk, const int64_t dk_strides[4],
+                   void* dv, const int64_t dv_strides[4], void* stream) {
+  // Argument checks first (no HIP call): fa_bwd's own, with a stand-in
+  // non-null workspace pointer that is never dereferenced by a rejected
+  // call, plus the scratch limit.
+  const int st = shape_check(B, H, Sq, Sk, D, dtype);
+  if (st != FA_OK) return st;
+  if (B > 0 && H > 0 && Sq > 0 && B * H * Sq > kScratchRows) return FA_ERR_WORKSPACE;
+  float* ws = nullptr;
+  if (B * H * Sq > 0 && Sk > 0) {
+    // Validate everything fa_bwd validates before touching the device.
+    const int pre = bwd_impl(-2, -1, -1, q, q_strides, k, k_strides, v, v_strides, o, o_strides,
+                             dout, dout_strides, lse, B, H, Sq, Sk, D, causal, scale, dtype,
+                             reinterpret_cast<float*>(uintptr_t(1)), dq, dq_strides, dk,
+                             dk_strides, dv, dv_strides, stream);
+    if (pre != FA_OK) return pre;
+    const int sst = scratch_for_current_device(&ws);
+    if (sst != FA_OK) return sst;
+  }
+  return bwd_impl(-1, -1, -1, q, q_strides, k, k_strides, v, v_strides, o, o_strides, dout,
+                  dout_strides, lse, B, H, Sq, Sk, D, causal, scale, dtype, ws, dq, dq_strides,
+                  dk, dk_strides, dv, dv_strides, stream);
+}
 
 int fa_fwd(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
            const void* v, const int64_t v_strides[4], int64_t B, int64_t H, int64_t Sq,
@@ -311,6 +375,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_TILE: return "FA_ERR_TILE: tile id out of range";
     case FA_ERR_CAUSAL: return "FA_ERR_CAUSAL: causal must be 0, 1 (top-left) or 2 (bottom-right)";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_WORKSPACE:
+      return "FA_ERR_WORKSPACE: B*H*Sq exceeds the allocation-free entry point's scratch (2^22 rows)";
   }
   return "unknown fa_status";
 }

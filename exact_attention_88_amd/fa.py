@@ -13,7 +13,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["FAError", "fa_fwd", "fa_bwd", "fa_fwd_tile", "fa_bwd_tile", "fa_bwd_stage", "fa_probe",
+__all__ = ["FAError", "fa_fwd", "fa_bwd", "fa_fwd_tile", "fa_bwd_tile", "fa_bwd_stage",
+           "fa_bwd_noalloc", "fa_probe",
            "fa_tile_count",
            "fa_tile_info", "fa_tile_default", "fa_status_string", "fa_last_hip_error", "fa_version",
            "lib_path",
@@ -24,8 +25,9 @@ FA_F16, FA_F32, FA_BF16 = 0, 1, 2
 FA_PASS_FWD, FA_PASS_BWD_DKDV, FA_PASS_BWD_DQ = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_fwd_tile", "fa_bwd_tile", "fa_bwd_stage",
-                    "fa_tile_count", "fa_tile_info", "fa_tile_default", "fa_status_string",
-                    "fa_last_hip_error", "fa_version", "fa_probe", "fa_probe_threads")
+                    "fa_bwd_noalloc", "fa_tile_count", "fa_tile_info", "fa_tile_default",
+                    "fa_status_string", "fa_last_hip_error", "fa_version", "fa_probe",
+                    "fa_probe_threads")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -72,7 +74,10 @@ def _load():
     lib.fa_bwd.argtypes = bwd_args
     lib.fa_bwd_tile.argtypes = [c_int, c_int] + bwd_args
     lib.fa_bwd_stage.argtypes = [c_int, c_int] + bwd_args
-    for name in ("fa_fwd", "fa_fwd_tile", "fa_bwd", "fa_bwd_tile", "fa_bwd_stage"):
+    # fa_bwd without the delta workspace (argument 19 of fa_bwd).
+    lib.fa_bwd_noalloc.argtypes = bwd_args[:19] + bwd_args[20:]
+    for name in ("fa_fwd", "fa_fwd_tile", "fa_bwd", "fa_bwd_tile", "fa_bwd_stage",
+                 "fa_bwd_noalloc"):
         getattr(lib, name).restype = c_int
     lib.fa_tile_count.argtypes = [c_int, c_int, i64]
     lib.fa_tile_count.restype = c_int
@@ -307,6 +312,27 @@ def fa_bwd(q, k, v, o, dout, lse, causal=False, scale=None, dq=None, dk=None, dv
            delta=None):
     """Backward attention: ``(dq, dk, dv, delta)``; see ``fa_bwd`` in include/fa.h."""
     return fa_bwd_tile(-1, -1, q, k, v, o, dout, lse, causal, scale, dq, dk, dv, delta)
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal=False, scale=None):
+    """``fa_bwd`` for callers that cannot allocate: the outputs ``dq``, ``dk``,
+    ``dv`` are required, and delta goes to the library's fixed per-device
+    scratch (B*H*Sq up to 2^22); see ``fa_bwd_noalloc`` in include/fa.h.
+    Returns ``(dq, dk, dv)``."""
+    _check_layout(q, k, v, (o, dout, dq), (dk, dv), (lse,))
+    _check_4d(q, k, v, o, dout, dq, dk, dv)
+    _check_same_device(q, lse)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if scale is None:
+        scale = D ** -0.5
+    st = _lib.fa_bwd_noalloc(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                             _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse), B, H,
+                             Sq, Sk, D, _causal_code(causal), float(scale), _dtype_code(q),
+                             _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv),
+                             _strides(dv), _stream_ptr(q))
+    _check(st)
+    return dq, dk, dv
 
 
 def fa_bwd_stage(stage, tile_id, q, k, v, o, dout, lse, causal=False, scale=None, dq=None,

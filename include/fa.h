@@ -73,10 +73,11 @@ typedef enum {
   FA_ERR_HIP = -6,    /* the HIP runtime reported an error at launch */
   FA_ERR_TILE = -7,   /* a forced tile id is out of range for this pass, dtype and D */
   FA_ERR_CAUSAL = -8, /* causal is not 0, 1 or 2 */
-  FA_ERR_SCALE = -9   /* scale is not a finite number > 0 (the kernels take the softmax over
+  FA_ERR_SCALE = -9,  /* scale is not a finite number > 0 (the kernels take the softmax over
                          scale * q.k in base 2 with the running max raised, never lowered, which
                          needs a positive scale; masked scores are -inf, so scale = 0 would give
                          0 * inf) */
+  FA_ERR_WORKSPACE = -10 /* fa_bwd_noalloc: B*H*Sq is larger than its fixed scratch (2^22 rows) */
 } fa_status;
 
 /* Pass ids for the tile-table queries. */
@@ -137,6 +138,34 @@ int fa_bwd(const void* q, const int64_t q_strides[4],
            void* dk, const int64_t dk_strides[4],
            void* dv, const int64_t dv_strides[4],
            void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and kernels as fa_bwd, without the
+ * delta_ws argument: delta = rowsum(dO o O) goes to a fixed scratch array
+ * of 2^22 floats (16 MiB) that the library holds in its own device globals,
+ * one per GPU, for the life of the process.  The call allocates nothing and
+ * frees nothing.  B*H*Sq above 2^22 is FA_ERR_WORKSPACE (checked before any
+ * HIP call, like every other argument).  The first call on a device looks up
+ * that device's scratch address once.  Nothing in the scratch needs to
+ * start at zero (delta is written before it is read, on `stream`), but the
+ * array is shared by every call on that GPU: calls that overlap on one GPU
+ * (different streams, or host threads) race on it and must be serialised by
+ * the caller.
+ */
+int fa_bwd_noalloc(const void* q, const int64_t q_strides[4],
+                   const void* k, const int64_t k_strides[4],
+                   const void* v, const int64_t v_strides[4],
+                   const void* o, const int64_t o_strides[4],
+                   const void* dout, const int64_t dout_strides[4],
+                   const float* lse,
+                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                   int causal, float scale, int dtype,
+                   void* dq, const int64_t dq_strides[4],
+                   void* dk, const int64_t dk_strides[4],
+                   void* dv, const int64_t dv_strides[4],
+                   void* stream);
 
 /*
  * Tile table ("Triton FlashAttention": block sizes tuned per power-of-two

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert "gfx950" in fa.fa_version()
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         assert fa.fa_status_string(code).startswith("FA_")
     assert "unknown" in fa.fa_status_string(-99)
 
@@ -204,3 +204,31 @@ def test_probe_rejects_bad_arguments_before_any_launch():
     assert lib.fa_probe(-1, 10, sink, None) == -2
     assert lib.fa_probe(0, 0, sink, None) == -2      # no iterations
     assert lib.fa_probe(1, 10, None, None) == -1     # no sink
+
+
+def _bwd_noalloc(B=1, H=1, Sq=8, Sk=8, D=64, dtype=0, causal=0, scale=0.125, ptrs=None):
+    p = dict(q=FAKE, k=FAKE + 1 * 4096, v=FAKE + 2 * 4096, o=FAKE + 3 * 4096,
+             do=FAKE + 4 * 4096, lse=FAKE + 5 * 4096, dq=FAKE + 7 * 4096, dk=FAKE + 8 * 4096,
+             dv=FAKE + 9 * 4096)
+    p.update(ptrs or {})
+    vp = ctypes.c_void_p
+    return lib.fa_bwd_noalloc(vp(p["q"]), S, vp(p["k"]), S, vp(p["v"]), S, vp(p["o"]), S,
+                              vp(p["do"]), S, vp(p["lse"]), B, H, Sq, Sk, D, causal,
+                              ctypes.c_float(scale), dtype, vp(p["dq"]), S, vp(p["dk"]), S,
+                              vp(p["dv"]), S, vp(0))
+
+
+def test_bwd_noalloc_validation_before_any_hip_call():
+    """The allocation-free backward checks what fa_bwd checks, and its scratch
+    limit (B*H*Sq <= 2^22), before touching the device."""
+    assert _bwd_noalloc(B=1, H=16, Sq=(1 << 18) + 1) == -10   # one row past the scratch
+    assert _bwd_noalloc(B=1 << 10, H=1 << 10, Sq=8) == -10
+    assert _bwd_noalloc(dtype=9) == -3
+    assert _bwd_noalloc(D=40) == -2
+    assert _bwd_noalloc(scale=0.0) == -9
+    assert _bwd_noalloc(causal=5) == -8
+    assert _bwd_noalloc(ptrs=dict(dq=0)) == -1
+    assert _bwd_noalloc(ptrs=dict(dk=FAKE)) == -5          # dk aliases q
+    assert _bwd_noalloc(B=0) == 0
+    assert _bwd_noalloc(Sq=0, Sk=0) == 0
+    assert "scratch" in fa.fa_status_string(-10)
