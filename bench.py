@@ -42,7 +42,6 @@ import argparse
 import json
 import os
 import statistics
-import subprocess
 import sys
 import threading
 import time
@@ -95,14 +94,6 @@ def make_device_inputs(case, torch):
 
 # ----------------------------------------------------------------- environment
 
-def _run(cmd, timeout=30):
-    try:
-        r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout)
-        return (r.stdout + r.stderr).strip()
-    except Exception as e:  # missing tool, timeout
-        return f"unavailable: {type(e).__name__}"
-
-
 def environment(fa, torch):
     """Toolchain and device of this run (compiler versions are part of the
     result: "Triton FlashAttention", takeaways)."""
@@ -114,13 +105,12 @@ def environment(fa, torch):
                 break
         except OSError:
             pass
-    hipcc = _run(["/opt/rocm/bin/hipcc", "--version"]).splitlines()
     props = torch.cuda.get_device_properties(0)
     return {
+        # name, HIP version and the compiler that built the library
         "library": fa.fa_version(),
         "library_source_sha": library_source_sha(),
         "rocm": rocm,
-        "hipcc": " | ".join(ln for ln in hipcc if ln.strip())[:300],
         "torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None),
         "device": props.name, "arch": getattr(props, "gcnArchName", ""),
         "compute_units": props.multi_processor_count,
@@ -232,22 +222,6 @@ class Sensors:
                 rec[key] = {"min": round(min(vals), 1), "median": round(statistics.median(vals), 1),
                             "max": round(max(vals), 1)}
         return rec
-
-
-def smi_snapshot():
-    """Clock and power as the system tools report them (one snapshot; the
-    first tool that answers)."""
-    for cmd in (["amd-smi", "metric", "-p", "-c", "--json"],
-                ["rocm-smi", "--showclocks", "--showpower", "--json"]):
-        out = _run(cmd, timeout=20)
-        starts = [i for i in (out.find("{"), out.find("[")) if i >= 0]
-        if out.startswith("unavailable") or not starts:
-            continue
-        try:
-            return {"tool": cmd[0], "data": json.loads(out[min(starts):])}
-        except ValueError:
-            return {"tool": cmd[0], "text": out[:600]}
-    return {"tool": None}
 
 
 def tiles_used(fa, case):
@@ -651,7 +625,6 @@ def main():
 
     env = environment(fa, torch)
     sensors = Sensors(env["pci_bus_id"])
-    smi_start = smi_snapshot()
     flush = Flusher(torch, enabled=not args.no_flush)
     case = W.long_case()
     if args.seq:
@@ -707,7 +680,7 @@ def main():
                      "traffic": measured_traffic(dom)},
         "tiles": tiles_used(fa, case),
         "environment": env,
-        "clock_power": {"during_timed_steps": r["sensors"], "smi_at_start": smi_start},
+        "clock_power": {"during_timed_steps": r["sensors"]},
     }
     if not args.no_bf16:
         # Secondary figure: the same workload in bfloat16 (inputs rounded to
@@ -736,7 +709,6 @@ def main():
         sweep, sweep_samples = length_sweep(fa, torch, max(10, args.steps), 20, flush,
                                             keep_samples=not args.no_cpu_baseline)
         line["length_sweep"] = sweep
-    line["clock_power"]["smi_at_end"] = smi_snapshot()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, x, args.cpu_heads, value)
         line["parity"] = parity_check(case, x, headline_samples)
