@@ -27,7 +27,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["fa_fwd.hip", "fa_fwd_f16.hip", "fa_bwd_dkdv.hip", "fa_bwd_dq.hip", "fa_bwd_f16.hip",
-           "fa_probe.hip", "fa_api.hip"]
+           "fa_bwd_split.hip", "fa_probe.hip", "fa_api.hip"]
 
 
 def hipcc() -> str:

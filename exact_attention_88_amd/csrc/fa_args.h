@@ -91,5 +91,10 @@ bool dq_fast_fuses_delta(const BwdArgs& a, int variant, int dtype);
 int dkdv_fast_variants();
 TileCfg dkdv_fast_cfg(int variant);
 hipError_t launch_dkdv_fast(const BwdArgs& a, int variant, int dtype, int causal, hipStream_t s);
+// dK/dV with each 32-key slice split over a score wave and an accumulate wave
+// (fa_bwd_split.hip).
+bool dkdv_split_fits(const BwdArgs& a, int esize);
+int dkdv_split_lds();
+hipError_t launch_dkdv_split(const BwdArgs& a, int dtype, int causal, hipStream_t s);
 
 }  // namespace fa

@@ -944,9 +944,13 @@ hipError_t launch_dq_fast(const BwdArgs& a, int v, int dtype, int causal, hipStr
 // 4 = variant 3 software-pipelined with buffer loads into LDS (variant 3 runs
 // instead where its 31-bit offsets do not reach every row).  (With 8 waves, two per SIMD, the
 // 32 keys' K, V, dK and dV no longer fit the 256 registers a wave then gets,
-// and the compiler spills.)
-int dkdv_fast_variants() { return 5; }
+// and the compiler spills.)  5 = 128 keys over 8 waves, each 32-key slice
+// split between a score wave (K, dV) and an accumulate wave (V, dK) that
+// trade P through LDS, 64-query tiles in three buffers (fa_bwd_split.hip;
+// variant 4 runs instead where its 31-bit offsets do not reach every row).
+int dkdv_fast_variants() { return 6; }
 TileCfg dkdv_fast_cfg(int v) {
+  if (v == 5) return TileCfg{64, 128, 8, dkdv_split_lds()};
   const int bm = v == 1 ? 32 : v >= 3 ? 128 : 64, nw = 4;
   const int row_halfs = v >= 2 ? 2 * kD : 2 * kLSR + 2 * kLST;
   return TileCfg{bm, 32 * nw, nw, 2 * bm * row_halfs * 2 + 2 * 2 * bm * 4};
@@ -961,6 +965,9 @@ hipError_t launch_dkdv_variant(const BwdArgs& a, int v, int causal, hipStream_t 
     case 4:
       if (!dkdv_pipe_fits(a, (int)sizeof(T))) return launch_dkdv_variant<T>(a, 3, causal, s);
       return causal ? launch_dkdv_pipe<T, true>(a, s) : launch_dkdv_pipe<T, false>(a, s);
+    case 5:
+      if (!dkdv_split_fits(a, (int)sizeof(T))) return launch_dkdv_variant<T>(a, 4, causal, s);
+      return launch_dkdv_split(a, std::is_same<T, bf16_t>::value ? 2 : 0, causal, s);
   }
   return hipErrorInvalidValue;
 }
