@@ -41,8 +41,10 @@ def hipcc() -> str:
 # error: spilling tile configurations are pruned from the tile tables.  The
 # exceptions are the generic fp32 head-dim-128 backward kernels, where every
 # candidate spills and the one that spills least is kept (mangled-name
-# fragments of the allowed instantiations).
-ALLOWED_SCRATCH = ("11dkdv_kernelIfLi128ELi32ELi4E", "9dq_kernelIfLi128ELi32ELi4ELb0E")
+# fragments of the allowed instantiations: the non-causal dK/dV kernel, and
+# the dQ kernel; the causal dK/dV kernel, which accumulates dK and dV in two
+# passes of two column blocks each, no longer spills).
+ALLOWED_SCRATCH = ("11dkdv_kernelIfLi128ELi32ELi4ELi1ELb0E", "9dq_kernelIfLi128ELi32ELi4ELi1E")
 
 
 def _scratch_kernels(remarks: str):

@@ -81,14 +81,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------- dK / dV
-struct Tile { int bm, nw; };
-constexpr Tile kTilesH[] = {{64, 4}, {32, 4}, {64, 2}, {128, 4}, {32, 8}};
-constexpr Tile kTilesF[] = {{32, 4}, {32, 2}, {64, 4}};
+// Query rows per tile, waves, and Q/dO buffers in LDS (1: load then compute,
+// two barriers per tile; 2: the next tile's global reads are issued into
+// registers before the current tile is computed and stored to the other
+// buffer after it, one barrier per tile).  New configurations go at the end
+// so that the ids of the existing ones do not move.
+struct Tile { int bm, nw, nb; };
+constexpr Tile kTilesH[] = {{64, 4, 1}, {32, 4, 1}, {64, 2, 1}, {128, 4, 1}, {32, 8, 1},
+                            {64, 4, 2}, {32, 4, 2}, {64, 2, 2}};
+constexpr Tile kTilesF[] = {{32, 4, 1}, {32, 2, 1}, {64, 4, 1}, {32, 4, 2}, {32, 2, 2}};
 constexpr int kNumH = sizeof(kTilesH) / sizeof(kTilesH[0]);
 constexpr int kNumF = sizeof(kTilesF) / sizeof(kTilesF[0]);
 
-constexpr int lds_bytes(int esize, int D, int bm) {
-  return 2 * bm * ((D < 32 ? 32 : D) + 16 / esize) * esize + 2 * bm * 4;
+constexpr int lds_bytes(int esize, int D, int bm, int nb) {
+  return nb * (2 * bm * ((D < 32 ? 32 : D) + 16 / esize) * esize + 2 * bm * 4);
 }
 constexpr Tile tile_at(int dt, int i) { return dt == 0 ? kTilesH[i] : kTilesF[i]; }
 constexpr int num_tiles_raw(int dt) { return dt == 0 ? kNumH : kNumF; }
@@ -98,7 +104,7 @@ constexpr int num_tiles_raw(int dt) { return dt == 0 ? kNumH : kNumF; }
 // spills least, is kept, so that fp32 D = 128 has a kernel.  The build fails
 // on any other kernel that uses scratch memory).
 constexpr bool tile_ok(int dt, int D, int i) {
-  return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bm) <= kLdsMax &&
+  return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bm, tile_at(dt, i).nb) <= kLdsMax &&
          !(D == 128 && dt == 0 && tile_at(dt, i).nw == 8) &&
          !(D == 128 && dt == 1 && tile_at(dt, i).nw == 2);
 }
@@ -118,25 +124,30 @@ constexpr int count_ok(int dt, int D) {
   return n;
 }
 
-template <class T, int D, int BM, int NW, bool CAUSAL>
+template <class T, int D, int BM, int NW, int NB, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
   typedef Mfma<T> M;
   constexpr int BN = 32 * NW;
   constexpr int NT = NW * 64;
   constexpr int LS = LdsRow<T, D>::LS;
   constexpr int NKS = D / M::KSTEP;
-  constexpr int NDB = (D + 31) / 32;
+  // fp32 at head dim 128: K and V fragments (128 registers) and the dK, dV
+  // accumulators of all four 32-column blocks (256) do not fit one wave, so
+  // the kernel runs twice over the queries, accumulating two column blocks
+  // of dK and dV each time (the scores are recomputed).
+  constexpr int NPASS = (sizeof(T) == 4 && D == 128) ? 2 : 1;
+  constexpr int NDB = (D + 31) / 32 / NPASS;  // 32-column blocks per pass
   constexpr int NQB = BM / 32;
   constexpr int TPB = 32 / M::KSTEP;
-  __shared__ __attribute__((aligned(16))) T Qs[BM * LS];
-  __shared__ __attribute__((aligned(16))) T Ds[BM * LS];
-  __shared__ float Ls[BM];
-  __shared__ float Dl[BM];
+  __shared__ __attribute__((aligned(16))) T Qs[NB][BM * LS];
+  __shared__ __attribute__((aligned(16))) T Ds[NB][BM * LS];
+  __shared__ float Ls[NB][BM];
+  __shared__ float Dl[NB][BM];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nkb = (a.Sk + BN - 1) / BN;
-  const int kb = blockIdx.x % nkb;
-  const int bh = blockIdx.x / nkb;
+  int kb, bh;
+  xcd_block(nkb, CAUSAL, kb, bh);  // a head's blocks on one XCD; causal key block 0 (the longest) first
   const int b = bh / a.H, h = bh % a.H;
   const int k0 = kb * BN, kw = k0 + w * 32, kj = kw + c;
 
@@ -152,40 +163,36 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
   load_row_frags<T, D>(vf, vbase, a.v.ss, a.v.sd, kj, a.Sk, a.vec & VEC_V);
 
   f32x16 dk[NDB], dv[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) { dk[i] = zero16(); dv[i] = zero16(); }
   const float cs = a.scale_log2;
   const bool vecq = a.vec & VEC_Q, vecd = a.vec & VEC_DO;
   const bool key_tail = k0 + BN > a.Sk;
+  int d0 = 0;  // first column of this pass's blocks
 
-  const int qstart = CAUSAL ? (max(0, k0 - a.coff) / BM) * BM : 0;
-  for (int q0 = qstart; q0 < a.Sq; q0 += BM) {
-    __syncthreads();
-    load_tile<T, BM, D, LS, NT>(Qs, qbase, a.q.ss, a.q.sd, q0, a.Sq, vecq);
-    load_tile<T, BM, D, LS, NT>(Ds, dobase, a.dout.ss, a.dout.sd, q0, a.Sq, vecd);
-    for (int r = threadIdx.x; r < BM; r += NT) {
-      const int i = q0 + r;
-      // fp16 kernels use LSE*log2(e); fp32 kernels use LSE itself.
-      // Rows past the end, and rows with no visible key (LSE = -inf), get P = 0.
-      const float li = i < a.Sq ? lse[i] : INFINITY;
-      Ls[r] = li == -INFINITY ? INFINITY : (sizeof(T) == 2 ? li * kLog2e : li);
-      Dl[r] = i < a.Sq ? dl[i] : 0.f;
-    }
-    __syncthreads();
+  // LSE (fp16 kernels: LSE*log2(e); fp32 kernels: LSE itself) and delta of
+  // tile row r.  Rows past the end, and rows with no visible key (LSE =
+  // -inf), get P = 0.
+  auto row_ls = [&](int i) {
+    const float li = i < a.Sq ? lse[i] : INFINITY;
+    return li == -INFINITY ? INFINITY : (sizeof(T) == 2 ? li * kLog2e : li);
+  };
+  auto row_dl = [&](int i) { return i < a.Sq ? dl[i] : 0.f; };
+
+  // One tile of BM query rows starting at q0, from LDS.
+  auto compute = [&](const T* Qt, const T* Dt, const float* Lt, const float* Mt, int q0) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qs = q0 + qb * 32;
       if (CAUSAL && qs + a.coff + 31 < kw) continue;  // every query of the block precedes every key
-      f32x16 s = dot_block<T, D, LS>(Qs, qb * 32, kf);
+      f32x16 s = dot_block<T, D, LS>(Qt, qb * 32, kf);
       const bool need_mask = key_tail || (CAUSAL && qs + a.coff < kw + 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qr = qb * 32 + crow(r, g);
         float p;
         if constexpr (sizeof(T) == 2)
-          p = fast_exp2(__builtin_fmaf(s[r], cs, -Ls[qr]));
+          p = fast_exp2(__builtin_fmaf(s[r], cs, -Lt[qr]));
         else
-          p = fast_exp2(__builtin_fmaf(a.scale, s[r], -Ls[qr]) * kLog2e);
+          p = fast_exp2(__builtin_fmaf(a.scale, s[r], -Lt[qr]) * kLog2e);
         if (need_mask && (kj >= a.Sk || (CAUSAL && kj > q0 + qr + a.coff))) p = 0.f;
         s[r] = p;
       }
@@ -194,28 +201,83 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
         const typename M::frag pf = frag_from_acc<T>(s, tt);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          dv[db] = M::mma(frag_tr<T, LS>(Ds, qb * 32, tt, db * 32), pf, dv[db]);
+          dv[db] = M::mma(frag_tr<T, LS>(Dt, qb * 32, tt, d0 + db * 32), pf, dv[db]);
       }
-      const f32x16 dp = dot_block<T, D, LS>(Ds, qb * 32, vf);
+      const f32x16 dp = dot_block<T, D, LS>(Dt, qb * 32, vf);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qr = qb * 32 + crow(r, g);
-        s[r] = s[r] * (dp[r] - Dl[qr]);
+        s[r] = s[r] * (dp[r] - Mt[qr]);
       }
 #pragma unroll
       for (int tt = 0; tt < TPB; ++tt) {
         const typename M::frag df = frag_from_acc<T>(s, tt);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          dk[db] = M::mma(frag_tr<T, LS>(Qs, qb * 32, tt, db * 32), df, dk[db]);
+          dk[db] = M::mma(frag_tr<T, LS>(Qt, qb * 32, tt, d0 + db * 32), df, dk[db]);
       }
+    }
+  };
+
+  const int qstart = CAUSAL ? (max(0, k0 - a.coff) / BM) * BM : 0;
+  T* dkrow = (T*)a.dk.p + b * a.dk.sb + h * a.dk.sh + (int64_t)kj * a.dk.ss;
+  T* dvrow = (T*)a.dv.p + b * a.dv.sb + h * a.dv.sh + (int64_t)kj * a.dv.ss;
+  const bool veck = a.vec & VEC_DK, vecv = a.vec & VEC_DV;
+  for (int pass = 0; pass < NPASS; ++pass) {
+  d0 = pass * NDB * 32;
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) { dk[i] = zero16(); dv[i] = zero16(); }
+  if (pass > 0) __syncthreads();  // the previous pass's last tile has been read
+  if constexpr (NB == 1) {
+    for (int q0 = qstart; q0 < a.Sq; q0 += BM) {
+      __syncthreads();
+      load_tile<T, BM, D, LS, NT>(Qs[0], qbase, a.q.ss, a.q.sd, q0, a.Sq, vecq);
+      load_tile<T, BM, D, LS, NT>(Ds[0], dobase, a.dout.ss, a.dout.sd, q0, a.Sq, vecd);
+      for (int r = threadIdx.x; r < BM; r += NT) {
+        Ls[0][r] = row_ls(q0 + r);
+        Dl[0][r] = row_dl(q0 + r);
+      }
+      __syncthreads();
+      compute(Qs[0], Ds[0], Ls[0], Dl[0], q0);
+    }
+  } else {
+    static_assert(BM <= NT, "one thread per staged LSE / delta row");
+    TileStage<T, BM, D, LS, NT> sq, sd;
+    float rl = 0.f, rd = 0.f;
+    const int r = threadIdx.x;
+    auto stage = [&](int q0) {
+      sq.load(qbase, a.q.ss, a.q.sd, q0, a.Sq, vecq);
+      sd.load(dobase, a.dout.ss, a.dout.sd, q0, a.Sq, vecd);
+      if (r < BM) {
+        rl = row_ls(q0 + r);
+        rd = row_dl(q0 + r);
+      }
+    };
+    auto put = [&](int buf) {
+      sq.store(Qs[buf]);
+      sd.store(Ds[buf]);
+      if (r < BM) {
+        Ls[buf][r] = rl;
+        Dl[buf][r] = rd;
+      }
+    };
+    const int ntiles = a.Sq > qstart ? (a.Sq - qstart + BM - 1) / BM : 0;
+    if (ntiles > 0) {
+      stage(qstart);
+      put(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int q0 = qstart + t * BM, cur = t & 1;
+      const bool more = t + 1 < ntiles;
+      if (more) stage(q0 + BM);
+      compute(Qs[cur], Ds[cur], Ls[cur], Dl[cur], q0);
+      if (more) put(cur ^ 1);  // the other buffer was last read before the previous barrier
+      __syncthreads();
     }
   }
 
   if (kj < a.Sk) {
-    T* dkrow = (T*)a.dk.p + b * a.dk.sb + h * a.dk.sh + (int64_t)kj * a.dk.ss;
-    T* dvrow = (T*)a.dv.p + b * a.dv.sb + h * a.dv.sh + (int64_t)kj * a.dv.ss;
-    const bool veck = a.vec & VEC_DK, vecv = a.vec & VEC_DV;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -226,10 +288,11 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
           k4[e] = dk[db][r4 * 4 + e] * a.scale;
           v4[e] = dv[db][r4 * 4 + e];
         }
-        store4<T, D>(dkrow, a.dk.sd, db * 32 + r4 * 8 + g * 4, k4, veck);
-        store4<T, D>(dvrow, a.dv.sd, db * 32 + r4 * 8 + g * 4, v4, vecv);
+        store4<T, D>(dkrow, a.dk.sd, d0 + db * 32 + r4 * 8 + g * 4, k4, veck);
+        store4<T, D>(dvrow, a.dv.sd, d0 + db * 32 + r4 * 8 + g * 4, v4, vecv);
       }
   }
+  }  // pass
 }
 
 template <class T, int D, int I, bool CAUSAL>
@@ -241,7 +304,7 @@ hipError_t launch_one(const BwdArgs& a, hipStream_t s) {
   const int64_t grid = nkb * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_kernel<T, D, tl.bm, tl.nw, CAUSAL>), dim3((unsigned)grid), dim3(tl.nw * 64), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_kernel<T, D, tl.bm, tl.nw, tl.nb, CAUSAL>), dim3((unsigned)grid), dim3(tl.nw * 64), args, 0, s);
 }
 
 template <class T, int D, int I = 0>
@@ -309,7 +372,7 @@ const TileCfg* dkdv_tile(int dtype, int D, int id) {
   }
   id -= nf;
   const Tile t = tile_at(table_dt(dtype), raw_for(dtype, D, id));
-  cfg = TileCfg{t.bm, 32 * t.nw, t.nw, lds_bytes(elem_size(dtype), D, t.bm)};
+  cfg = TileCfg{t.bm, 32 * t.nw, t.nw, lds_bytes(elem_size(dtype), D, t.bm, t.nb)};
   return &cfg;
 }
 

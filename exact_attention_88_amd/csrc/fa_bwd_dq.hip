@@ -24,14 +24,20 @@ namespace {
 
 constexpr int kLdsMax = 65536;
 
-struct Tile { int bn, nw; };
-constexpr Tile kTilesH[] = {{64, 4}, {32, 4}, {64, 2}, {128, 4}, {64, 8}};
-constexpr Tile kTilesF[] = {{32, 4}, {32, 2}, {64, 4}};
+// Keys per tile, waves, and K/V buffers in LDS (1: load then compute, two
+// barriers per tile; 2: the next tile's global reads are issued into
+// registers before the current tile is computed and stored to the other
+// buffer after it, one barrier per tile).  New configurations go at the end
+// so that the ids of the existing ones do not move.
+struct Tile { int bn, nw, nb; };
+constexpr Tile kTilesH[] = {{64, 4, 1}, {32, 4, 1}, {64, 2, 1}, {128, 4, 1}, {64, 8, 1},
+                            {64, 4, 2}, {32, 4, 2}, {64, 8, 2}};
+constexpr Tile kTilesF[] = {{32, 4, 1}, {32, 2, 1}, {64, 4, 1}, {32, 4, 2}};
 constexpr int kNumH = sizeof(kTilesH) / sizeof(kTilesH[0]);
 constexpr int kNumF = sizeof(kTilesF) / sizeof(kTilesF[0]);
 
-constexpr int lds_bytes(int esize, int D, int bn) {
-  return 2 * bn * ((D < 32 ? 32 : D) + 16 / esize) * esize;
+constexpr int lds_bytes(int esize, int D, int bn, int nb) {
+  return nb * 2 * bn * ((D < 32 ? 32 : D) + 16 / esize) * esize;
 }
 constexpr Tile tile_at(int dt, int i) { return dt == 0 ? kTilesH[i] : kTilesF[i]; }
 constexpr int num_tiles_raw(int dt) { return dt == 0 ? kNumH : kNumF; }
@@ -41,7 +47,7 @@ constexpr int num_tiles_raw(int dt) { return dt == 0 ? kNumH : kNumF; }
 // little when non-causal and is kept, so that fp32 D = 128 has a kernel.  The
 // build fails on any other kernel that uses scratch memory).
 constexpr bool tile_ok(int dt, int D, int i) {
-  return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bn) <= kLdsMax &&
+  return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bn, tile_at(dt, i).nb) <= kLdsMax &&
          !(D == 128 && dt == 0 && tile_at(dt, i).nw == 8) &&
          !(D == 128 && dt == 1 && tile_at(dt, i).nw == 2);
 }
@@ -61,7 +67,7 @@ constexpr int count_ok(int dt, int D) {
   return n;
 }
 
-template <class T, int D, int BN, int NW, bool CAUSAL>
+template <class T, int D, int BN, int NW, int NB, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
   typedef Mfma<T> M;
   constexpr int BM = 32 * NW;
@@ -71,14 +77,14 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
   constexpr int NDB = (D + 31) / 32;
   constexpr int NKB = BN / 32;
   constexpr int TPB = 32 / M::KSTEP;
-  __shared__ __attribute__((aligned(16))) T Ks[BN * LS];
-  __shared__ __attribute__((aligned(16))) T Vs[BN * LS];
+  __shared__ __attribute__((aligned(16))) T Ks[NB][BN * LS];
+  __shared__ __attribute__((aligned(16))) T Vs[NB][BN * LS];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nqb = (a.Sq + BM - 1) / BM;
-  int qb = blockIdx.x % nqb;
-  const int bh = blockIdx.x / nqb;
-  if (CAUSAL) qb = nqb - 1 - qb;
+  int qb, bh;
+  xcd_block(nqb, CAUSAL, qb, bh);  // a head's blocks on one XCD (its L2 holds their K/V)
+  if (CAUSAL) qb = nqb - 1 - qb;    // longest rows first
   const int b = bh / a.H, h = bh % a.H;
   const int q0 = qb * BM, qw = q0 + w * 32, qi = qw + c;
 
@@ -106,17 +112,13 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
 
   const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
   const int ntiles = (kend + BN - 1) / BN;
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * BN;
-    __syncthreads();
-    load_tile<T, BN, D, LS, NT>(Ks, kbase, a.k.ss, a.k.sd, k0, a.Sk, veck);
-    load_tile<T, BN, D, LS, NT>(Vs, vbase, a.v.ss, a.v.sd, k0, a.Sk, vecv);
-    __syncthreads();
+  // One tile: per 32-key block, P, dS and dQ += dS K, from LDS.
+  auto compute = [&](const T* Kt, const T* Vt, int k0) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int ks0 = k0 + kb * 32;
       if (CAUSAL && ks0 > qw + a.coff + 31) continue;  // block entirely after this wave's rows
-      f32x16 s = dot_block<T, D, LS>(Ks, kb * 32, qf);
+      f32x16 s = dot_block<T, D, LS>(Kt, kb * 32, qf);
       const bool need_mask = (ks0 + 32 > a.Sk) || (CAUSAL && ks0 + 31 > qw + a.coff);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
         if (need_mask && (key >= a.Sk || (CAUSAL && key > qi + a.coff))) p = 0.f;
         s[r] = p;
       }
-      const f32x16 dp = dot_block<T, D, LS>(Vs, kb * 32, df);
+      const f32x16 dp = dot_block<T, D, LS>(Vt, kb * 32, df);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - dlt);
 #pragma unroll
@@ -137,8 +139,41 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
         const typename M::frag sf = frag_from_acc<T>(s, tt);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          dq[db] = M::mma(frag_tr<T, LS>(Ks, kb * 32, tt, db * 32), sf, dq[db]);
+          dq[db] = M::mma(frag_tr<T, LS>(Kt, kb * 32, tt, db * 32), sf, dq[db]);
       }
+    }
+  };
+  if constexpr (NB == 1) {
+    for (int t = 0; t < ntiles; ++t) {
+      const int k0 = t * BN;
+      __syncthreads();
+      load_tile<T, BN, D, LS, NT>(Ks[0], kbase, a.k.ss, a.k.sd, k0, a.Sk, veck);
+      load_tile<T, BN, D, LS, NT>(Vs[0], vbase, a.v.ss, a.v.sd, k0, a.Sk, vecv);
+      __syncthreads();
+      compute(Ks[0], Vs[0], k0);
+    }
+  } else {
+    TileStage<T, BN, D, LS, NT> sk, sv;
+    if (ntiles > 0) {
+      sk.load(kbase, a.k.ss, a.k.sd, 0, a.Sk, veck);
+      sv.load(vbase, a.v.ss, a.v.sd, 0, a.Sk, vecv);
+      sk.store(Ks[0]);
+      sv.store(Vs[0]);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int k0 = t * BN, cur = t & 1;
+      const bool more = t + 1 < ntiles;
+      if (more) {
+        sk.load(kbase, a.k.ss, a.k.sd, k0 + BN, a.Sk, veck);
+        sv.load(vbase, a.v.ss, a.v.sd, k0 + BN, a.Sk, vecv);
+      }
+      compute(Ks[cur], Vs[cur], k0);
+      if (more) {  // the other buffer was last read before the previous barrier
+        sk.store(Ks[cur ^ 1]);
+        sv.store(Vs[cur ^ 1]);
+      }
+      __syncthreads();
     }
   }
 
@@ -166,7 +201,7 @@ hipError_t launch_one(const BwdArgs& a, hipStream_t s) {
   const int64_t grid = nqb * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_kernel<T, D, tl.bn, tl.nw, CAUSAL>), dim3((unsigned)grid), dim3(tl.nw * 64), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_kernel<T, D, tl.bn, tl.nw, tl.nb, CAUSAL>), dim3((unsigned)grid), dim3(tl.nw * 64), args, 0, s);
 }
 
 template <class T, int D, int I = 0>
@@ -224,7 +259,7 @@ const TileCfg* dq_tile(int dtype, int D, int id) {
   }
   id -= nf;
   const Tile t = tile_at(table_dt(dtype), raw_for(dtype, D, id));
-  cfg = TileCfg{32 * t.nw, t.bn, t.nw, lds_bytes(elem_size(dtype), D, t.bn)};
+  cfg = TileCfg{32 * t.nw, t.bn, t.nw, lds_bytes(elem_size(dtype), D, t.bn, t.nb)};
   return &cfg;
 }
 

@@ -147,6 +147,51 @@ __device__ __forceinline__ void load_tile(T* __restrict__ lds, const T* __restri
   }
 }
 
+// The same tile load split in two, for double buffering: load() issues the
+// global reads of rows [row0, row0 + ROWS) into registers (rows >= nrows give
+// zeros), store() writes them to LDS later, so the reads of tile t+1 are in
+// flight while tile t is computed.
+template <class T, int ROWS, int D, int LS, int NT>
+struct TileStage {
+  static constexpr int CH = 16 / (int)sizeof(T);
+  static constexpr int CPR = D / CH;
+  static constexpr int TOTAL = ROWS * CPR;
+  static constexpr int PER = (TOTAL + NT - 1) / NT;
+  uint4 r[PER];
+
+  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ss, int64_t sd, int row0,
+                                       int nrows, bool vec) {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = it * NT + (int)threadIdx.x;
+      r[it] = make_uint4(0u, 0u, 0u, 0u);
+      if (TOTAL % NT == 0 || c < TOTAL) {
+        const int row = row0 + c / CPR, col = (c % CPR) * CH;
+        if (row < nrows) {
+          const T* src = base + (int64_t)row * ss;
+          if (vec) {
+            r[it] = *reinterpret_cast<const uint4*>(src + col);
+          } else {
+            T tmp[CH];
+#pragma unroll
+            for (int e = 0; e < CH; ++e) tmp[e] = src[(int64_t)(col + e) * sd];
+            __builtin_memcpy(&r[it], tmp, 16);
+          }
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(T* __restrict__ lds) const {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = it * NT + (int)threadIdx.x;
+      if (TOTAL % NT == 0 || c < TOTAL)
+        *reinterpret_cast<uint4*>(lds + (c / CPR) * LS + (c % CPR) * CH) = r[it];
+    }
+  }
+};
+
 // Register fragments of rows of a strided [S][D] matrix, laid out as the B
 // operand of X^T (or the A operand of X): lane holds
 // X[row][ks*KSTEP + g*KPL + e] in frag[ks].  Rows >= nrows give zeros.

@@ -21,14 +21,20 @@ namespace {
 
 constexpr int kLdsMax = 65536;
 
-struct FwdTile { int bn, nw; };
-constexpr FwdTile kTilesH[] = {{64, 4}, {32, 4}, {64, 2}, {64, 8}, {128, 4}};
-constexpr FwdTile kTilesF[] = {{32, 4}, {32, 2}, {64, 4}, {32, 8}};
+// Keys per tile, waves, and K/V buffers in LDS (1: load then compute, two
+// barriers per tile; 2: the next tile's global reads are issued into
+// registers before the current tile is computed and stored to the other
+// buffer after it, one barrier per tile).  New configurations go at the end
+// so that the ids of the existing ones do not move.
+struct FwdTile { int bn, nw, nb; };
+constexpr FwdTile kTilesH[] = {{64, 4, 1}, {32, 4, 1}, {64, 2, 1}, {64, 8, 1}, {128, 4, 1},
+                               {64, 4, 2}, {32, 4, 2}, {64, 8, 2}};
+constexpr FwdTile kTilesF[] = {{32, 4, 1}, {32, 2, 1}, {64, 4, 1}, {32, 8, 1}, {32, 4, 2}, {32, 2, 2}};
 constexpr int kNumH = sizeof(kTilesH) / sizeof(kTilesH[0]);
 constexpr int kNumF = sizeof(kTilesF) / sizeof(kTilesF[0]);
 
-constexpr int lds_bytes(int esize, int D, int bn) {
-  return 2 * bn * ((D < 32 ? 32 : D) + 16 / esize) * esize;
+constexpr int lds_bytes(int esize, int D, int bn, int nb) {
+  return nb * 2 * bn * ((D < 32 ? 32 : D) + 16 / esize) * esize;
 }
 constexpr FwdTile tile_at(int dt, int i) { return dt == 0 ? kTilesH[i] : kTilesF[i]; }
 constexpr int num_tiles_raw(int dt) { return dt == 0 ? kNumH : kNumF; }
@@ -36,7 +42,7 @@ constexpr int num_tiles_raw(int dt) { return dt == 0 ? kNumH : kNumF; }
 // (measured with hipcc for gfx950: the fp32 head-dim-128 kernel with 8 waves
 // spills; the build fails on any other kernel that uses scratch memory).
 constexpr bool tile_ok(int dt, int D, int i) {
-  return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bn) <= kLdsMax &&
+  return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bn, tile_at(dt, i).nb) <= kLdsMax &&
          !(dt == 1 && D == 128 && tile_at(dt, i).nw == 8);
 }
 // Map compact id (among fitting tiles) -> raw index, or -1.
@@ -56,7 +62,7 @@ constexpr int count_ok(int dt, int D) {
   return n;
 }
 
-template <class T, int D, int BN, int NW, bool CAUSAL>
+template <class T, int D, int BN, int NW, int NB, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   typedef Mfma<T> M;
   constexpr int BM = 32 * NW;
@@ -66,13 +72,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   constexpr int NDB = (D + 31) / 32;     // 32-row blocks of O^T
   constexpr int NKB = BN / 32;           // 32-key blocks per tile
   constexpr int TPB = 32 / M::KSTEP;     // k-steps per 32-key block in P V
-  __shared__ __attribute__((aligned(16))) T Ks[BN * LS];
-  __shared__ __attribute__((aligned(16))) T Vs[BN * LS];
+  __shared__ __attribute__((aligned(16))) T Ks[NB][BN * LS];
+  __shared__ __attribute__((aligned(16))) T Vs[NB][BN * LS];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
   const int nqb = (a.Sq + BM - 1) / BM;
-  int qb = blockIdx.x % nqb;
-  const int bh = blockIdx.x / nqb;
+  int qb, bh;
+  xcd_block(nqb, CAUSAL, qb, bh);  // a head's blocks on one XCD (its L2 holds their K/V)
   if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
   const int b = bh / a.H, h = bh % a.H;
 
@@ -96,17 +102,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   const int ntiles = (kend + BN - 1) / BN;
   const bool veck = a.vec & VEC_K, vecv = a.vec & VEC_V;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * BN;
-    __syncthreads();
-    load_tile<T, BN, D, LS, NT>(Ks, kbase, a.k.ss, a.k.sd, k0, a.Sk, veck);
-    load_tile<T, BN, D, LS, NT>(Vs, vbase, a.v.ss, a.v.sd, k0, a.Sk, vecv);
-    __syncthreads();
-    if (CAUSAL && k0 > qw + a.coff + 31) continue;  // every key of the tile is after every row of this wave
-
+  // One tile's scores, online-softmax update and O += P V, from LDS.
+  auto compute = [&](const T* Kt, const T* Vt, int k0) {
     f32x16 s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = dot_block<T, D, LS>(Ks, kb * 32, qf);
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = dot_block<T, D, LS>(Kt, kb * 32, qf);
     const bool need_mask = (k0 + BN > a.Sk) || (CAUSAL && k0 + BN - 1 > qw + a.coff);
     if (need_mask) {
 #pragma unroll
@@ -156,8 +156,44 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
         const typename M::frag pf = frag_from_acc<T>(s[kb], tt);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          oacc[db] = M::mma(frag_tr<T, LS>(Vs, kb * 32, tt, db * 32), pf, oacc[db]);
+          oacc[db] = M::mma(frag_tr<T, LS>(Vt, kb * 32, tt, db * 32), pf, oacc[db]);
       }
+  };
+
+  if constexpr (NB == 1) {
+    for (int t = 0; t < ntiles; ++t) {
+      const int k0 = t * BN;
+      __syncthreads();
+      load_tile<T, BN, D, LS, NT>(Ks[0], kbase, a.k.ss, a.k.sd, k0, a.Sk, veck);
+      load_tile<T, BN, D, LS, NT>(Vs[0], vbase, a.v.ss, a.v.sd, k0, a.Sk, vecv);
+      __syncthreads();
+      if (CAUSAL && k0 > qw + a.coff + 31) continue;  // every key of the tile is after every row of this wave
+      compute(Ks[0], Vs[0], k0);
+    }
+  } else {
+    TileStage<T, BN, D, LS, NT> sk, sv;
+    if (ntiles > 0) {
+      sk.load(kbase, a.k.ss, a.k.sd, 0, a.Sk, veck);
+      sv.load(vbase, a.v.ss, a.v.sd, 0, a.Sk, vecv);
+      sk.store(Ks[0]);
+      sv.store(Vs[0]);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int k0 = t * BN, cur = t & 1;
+      const bool more = t + 1 < ntiles;
+      if (more) {
+        sk.load(kbase, a.k.ss, a.k.sd, k0 + BN, a.Sk, veck);
+        sv.load(vbase, a.v.ss, a.v.sd, k0 + BN, a.Sk, vecv);
+      }
+      // A wave whose rows all precede the tile still stages and syncs.
+      if (!(CAUSAL && k0 > qw + a.coff + 31)) compute(Ks[cur], Vs[cur], k0);
+      if (more) {  // the other buffer was last read before the previous barrier
+        sk.store(Ks[cur ^ 1]);
+        sv.store(Vs[cur ^ 1]);
+      }
+      __syncthreads();
+    }
   }
 
   const float ltot = lsum + xor32(lsum);
@@ -191,7 +227,7 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t s) {
   const int64_t grid = nqb * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<T, D, tl.bn, tl.nw, CAUSAL>), dim3((unsigned)grid), dim3(tl.nw * 64), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<T, D, tl.bn, tl.nw, tl.nb, CAUSAL>), dim3((unsigned)grid), dim3(tl.nw * 64), args, 0, s);
 }
 
 template <class T, int D, int I = 0>
@@ -251,7 +287,7 @@ const TileCfg* fwd_tile(int dtype, int D, int id) {
   }
   const int raw = raw_for(dtype, D, id - nf);
   const FwdTile t = tile_at(table_dt(dtype), raw);
-  cfg = TileCfg{32 * t.nw, t.bn, t.nw, lds_bytes(elem_size(dtype), D, t.bn)};
+  cfg = TileCfg{32 * t.nw, t.bn, t.nw, lds_bytes(elem_size(dtype), D, t.bn, t.nb)};
   return &cfg;
 }
 
