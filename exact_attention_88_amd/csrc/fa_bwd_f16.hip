@@ -440,22 +440,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   const float* dl = a.delta + (int64_t)bh * a.Sq;
   const int k0 = kb * BN, kw = k0 + w * 32, kj = kw + c;
 
-  V8<T> kf[8], vf[8];
-  {
-    const int kc = min(kj, a.Sk - 1);
-    const T* krow = (const T*)a.k.p + b * a.k.sb + h * a.k.sh + (int64_t)kc * a.k.ss;
-    const T* vrow = (const T*)a.v.p + b * a.v.sb + h * a.v.sh + (int64_t)kc * a.v.ss;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      kf[ks] = *reinterpret_cast<const V8<T>*>(krow + ks * 16 + g * 8);
-      vf[ks] = *reinterpret_cast<const V8<T>*>(vrow + ks * 16 + g * 8);
-    }
-  }
-  // K and V resident before any buffer load into LDS is issued: the compiler
-  // does not count those loads, so a wait it places for K or V later would
-  // also wait for them.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { dk[i] = zero16(); dv[i] = zero16(); }
@@ -506,10 +490,25 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int db = 0; db < 4; ++db) qtp[tt][db] = sf0;
+  // The first tile's buffer loads go out before the K and V row loads, so
+  // that the prologue waits for one memory round trip, not two.  (Loads
+  // issued after them complete after them, so the compiler's own waits for
+  // the rows, which do not count these loads, are conservative.)
+  if (ntiles > 0) issue_tile(0, 0);
+  V8<T> kf[8], vf[8];
+  {
+    const int kc = min(kj, a.Sk - 1);
+    const T* krow = (const T*)a.k.p + b * a.k.sb + h * a.k.sh + (int64_t)kc * a.k.ss;
+    const T* vrow = (const T*)a.v.p + b * a.v.sb + h * a.v.sh + (int64_t)kc * a.v.ss;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      kf[ks] = *reinterpret_cast<const V8<T>*>(krow + ks * 16 + g * 8);
+      vf[ks] = *reinterpret_cast<const V8<T>*>(vrow + ks * 16 + g * 8);
+    }
+  }
   if (ntiles > 0) {
-    issue_tile(0, 0);
     store_rows(0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): rows and this wave's buffer loads are in
     __syncthreads();
     if (ntiles > 1) issue_tile(1, 1);
 #pragma unroll
@@ -712,9 +711,12 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
 // instruction per element) instead of holding it splatted as the dP start
 // value, and from a compile-time buffer parity (immediate LDS offsets).
 // Needs the 31-bit offsets the dK/dV kernel needs, for K and V.
-template <class T, bool CAUSAL>
-__global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
-  constexpr int NW = 8, BM = 32 * NW, BN = 64, NT = NW * 64, NKB = BN / 32;
+// NW waves of 32 query rows: 8, or 4 so that two workgroups share a CU and
+// one's prologue and epilogue overlap the other's tiles (either way two waves
+// per SIMD).
+template <class T, bool CAUSAL, int NW = 8>
+__global__ __launch_bounds__(NW * 64, 2) void dq_pipe_d128(BwdArgs a) {
+  constexpr int BM = 32 * NW, BN = 64, NT = NW * 64, NKB = BN / 32;
   constexpr int TR = BN * kD, BUF = 2 * TR;  // K rows, V rows
   __shared__ __attribute__((aligned(1024))) T smem[2 * BUF];
   (void)NT;
@@ -734,6 +736,22 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
   const rsrc_t rv = make_rsrc(vbase, (int)((int64_t)a.Sk * a.v.ss * (int64_t)sizeof(T)));
   const int q0 = qb * BM, qw = q0 + w * 32, qi = qw + c;
   const bool valid = qi < a.Sq;
+
+  const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
+  const int ntiles = (kend + BN - 1) / BN;
+  const unsigned lds0 = lds_addr(smem);
+  const int ksb = (int)(a.k.ss * (int64_t)sizeof(T)), vsb = (int)(a.v.ss * (int64_t)sizeof(T));
+  const int klo = dma_lane_off<NW>(ksb), vlo = dma_lane_off<NW>(vsb);
+  auto issue_tile = [&](int t) {
+    const unsigned base = lds0 + (unsigned)((t & 1) * BUF * (int)sizeof(T));
+    tile_dma<BN, NW>(rk, base, klo, ksb, t * BN);
+    tile_dma<BN, NW>(rv, base + (unsigned)(TR * (int)sizeof(T)), vlo, vsb, t * BN);
+  };
+  // The first tile's buffer loads go out before the row loads, so that the
+  // prologue waits for one memory round trip, not two.  (The row loads
+  // issued after them complete after them, so the compiler's own waits for
+  // the rows, which do not count these loads, are conservative.)
+  if (ntiles > 0) issue_tile(0);
 
   V8<T> qf[8], df[8];
   const int qc = min(qi, a.Sq - 1);
@@ -770,27 +788,12 @@ __global__ __launch_bounds__(512, 2) void dq_pipe_d128(BwdArgs a) {
   } else {
     dlt = valid ? a.delta[(int64_t)bh * a.Sq + qi] : 0.f;
   }
-  // Row data resident before any buffer load into LDS is issued (the compiler
-  // does not count those).
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-
   f32x16 dq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = zero16();
   const float cs = a.scale_log2;
 
-  const int kend = CAUSAL ? max(0, min(a.Sk, q0 + a.coff + BM)) : a.Sk;
-  const int ntiles = (kend + BN - 1) / BN;
-  const unsigned lds0 = lds_addr(smem);
-  const int ksb = (int)(a.k.ss * (int64_t)sizeof(T)), vsb = (int)(a.v.ss * (int64_t)sizeof(T));
-  const int klo = dma_lane_off<NW>(ksb), vlo = dma_lane_off<NW>(vsb);
-  auto issue_tile = [&](int t) {
-    const unsigned base = lds0 + (unsigned)((t & 1) * BUF * (int)sizeof(T));
-    tile_dma<BN, NW>(rk, base, klo, ksb, t * BN);
-    tile_dma<BN, NW>(rv, base + (unsigned)(TR * (int)sizeof(T)), vlo, vsb, t * BN);
-  };
-  if (ntiles > 0) issue_tile(0);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): rows and this wave's first-tile loads are in
   __syncthreads();
 
   // Tile t reads buffer t & 1, a compile-time constant below (the loop is
@@ -878,13 +881,13 @@ bool dq_pipe_fits(const BwdArgs& a, int esize) {
          ((int64_t)a.Sk + 3 * 64) * a.v.ss * esize < lim;
 }
 
-template <class T, bool CAUSAL>
+template <class T, bool CAUSAL, int NW = 8>
 hipError_t launch_dq_pipe(const BwdArgs& a, hipStream_t s) {
-  const int64_t grid = (((int64_t)a.Sq + 255) / 256) * a.B * a.H;
+  const int64_t grid = (((int64_t)a.Sq + 32 * NW - 1) / (32 * NW)) * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_pipe_d128<T, CAUSAL>),
-                         dim3((unsigned)grid), dim3(512), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_pipe_d128<T, CAUSAL, NW>),
+                         dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
 }
 
 bool dkdv_pipe_fits(const BwdArgs& a, int esize) {
@@ -909,9 +912,11 @@ hipError_t launch_dkdv_pipe(const BwdArgs& a, hipStream_t s) {
 // 4 with buffer loads into LDS and dP starting from -delta (variant 4 runs
 // instead where its 31-bit offsets do not reach every row).  (With 128-key
 // tiles the staging registers push the non-causal kernel into spills.)
-int dq_fast_variants() { return 6; }
+// 6 = variant 5 with 4 waves, 128 query rows per workgroup and two workgroups
+// per CU (variant 1 runs instead where the offsets do not reach).
+int dq_fast_variants() { return 7; }
 TileCfg dq_fast_cfg(int v) {
-  const int bn = v == 2 || v == 3 ? 32 : 64, nw = v == 1 ? 4 : 8;
+  const int bn = v == 2 || v == 3 ? 32 : 64, nw = v == 1 || v == 6 ? 4 : 8;
   const int row_halfs = v >= 3 ? 2 * kD : 2 * kLSR + kLST;
   return TileCfg{32 * nw, bn, nw, 2 * bn * row_halfs * 2};
 }
@@ -926,13 +931,16 @@ hipError_t launch_dq_variant(const BwdArgs& a, int v, int causal, hipStream_t s)
     case 5:
       if (!dq_pipe_fits(a, (int)sizeof(T))) return launch_dq_variant<T>(a, 4, causal, s);
       return causal ? launch_dq_pipe<T, true>(a, s) : launch_dq_pipe<T, false>(a, s);
+    case 6:
+      if (!dq_pipe_fits(a, (int)sizeof(T))) return launch_dq_variant<T>(a, 1, causal, s);
+      return causal ? launch_dq_pipe<T, true, 4>(a, s) : launch_dq_pipe<T, false, 4>(a, s);
   }
   return hipErrorInvalidValue;
 }
-// Variant 5 runs dq_pipe_d128 where its 31-bit offsets reach every row: that
-// kernel can form delta itself.
+// Variants 5 and 6 run dq_pipe_d128 where its 31-bit offsets reach every row:
+// that kernel can form delta itself.
 bool dq_fast_fuses_delta(const BwdArgs& a, int v, int dtype) {
-  return v == 5 && dq_pipe_fits(a, dtype == 1 ? 4 : 2);
+  return (v == 5 || v == 6) && dq_pipe_fits(a, dtype == 1 ? 4 : 2);
 }
 hipError_t launch_dq_fast(const BwdArgs& a, int v, int dtype, int causal, hipStream_t s) {
   if (dtype == 2) return launch_dq_variant<bf16_t>(a, v, causal, s);

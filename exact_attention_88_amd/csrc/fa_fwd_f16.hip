@@ -511,9 +511,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
 //     with K(t+3) and V(t+2) right after it.
 // Needs 31-bit byte offsets for every K and V row below Sk + 4*64 and a row
 // stride of at least 128 elements (checked on the host).
-template <class T, bool CAUSAL>
-__global__ __launch_bounds__(512, 2) void fwd_dma_d128(FwdArgs a) {
-  constexpr int NW = 8, BM = 32 * NW, BN = 64, TR = BN * kD;
+// NW waves of 32 query rows (8, or 4 so that two workgroups share a CU and
+// one's prologue and epilogue overlap the other's tiles; either way two
+// waves per SIMD).
+template <class T, bool CAUSAL, int NW = 8>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_dma_d128(FwdArgs a) {
+  static_assert(NW == 4 || NW == 8, "buffer loads move whole multiples of 16 rows");
+  constexpr int BM = 32 * NW, BN = 64, TR = BN * kD;
   __shared__ __attribute__((aligned(1024))) T smem[4 * TR];  // K0 K1 V0 V1
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
@@ -800,6 +804,10 @@ hipError_t launch_variant(const FwdArgs& a, int variant, int causal, hipStream_t
       if (!fwd_dma_fits(a, (int)sizeof(T))) return launch_pipe<T, 64, 8, true>(a, causal, s);
       return causal ? launch_k(&fwd_dma_d128<T, true>, 256, 512, a, s)
                     : launch_k(&fwd_dma_d128<T, false>, 256, 512, a, s);
+    case 5:
+      if (!fwd_dma_fits(a, (int)sizeof(T))) return launch_plain<T, 64, 4>(a, causal, s);
+      return causal ? launch_k(&fwd_dma_d128<T, true, 4>, 128, 256, a, s)
+                    : launch_k(&fwd_dma_d128<T, false, 4>, 128, 256, a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -809,12 +817,14 @@ hipError_t launch_variant(const FwdArgs& a, int variant, int causal, hipStream_t
 // Variants (BN keys per tile, waves): pipelined 0 = (64, 8, ordered),
 // 1 = (64, 8); plain 2 = (64, 8), 3 = (64, 4); 4 = pipelined (64, 8) with
 // buffer loads into LDS (variant 0 runs instead where its 31-bit offsets do
-// not reach every row).
-int fwd_fast_variants() { return 5; }
+// not reach every row); 5 = variant 4 with 4 waves, 128 query rows per
+// workgroup and two workgroups per CU (variant 3 runs instead where the
+// offsets do not reach).
+int fwd_fast_variants() { return 6; }
 
 TileCfg fwd_fast_cfg(int v) {
-  const int nw = v == 3 ? 4 : 8;
-  if (v == 4) return TileCfg{256, 64, 8, 4 * 64 * kD * 2};
+  const int nw = v == 3 || v == 5 ? 4 : 8;
+  if (v >= 4) return TileCfg{32 * nw, 64, nw, 4 * 64 * kD * 2};
   return TileCfg{32 * nw, 64, nw, 2 * 64 * (kLSK + kLSV) * 2};
 }
 
