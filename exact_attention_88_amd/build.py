@@ -26,6 +26,12 @@ FLAGS = [
     "-Wno-unused-result", "-ffp-contract=fast",
     "-I", os.path.join(ROOT, "include"),
 ]
+# Per-file flags.  fa_bwd_f16.hip: every MFMA takes the form whose accumulator
+# (C and D) is in architectural VGPRs, also in its one-wave-per-SIMD dK/dV
+# kernels, whose 512-register budget would otherwise put every product in
+# accumulator registers and read each score and dP element back with a
+# v_accvgpr_read; those kernels keep K and V in accumulator registers instead.
+EXTRA_FLAGS = {"fa_bwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 SOURCES = ["fa_fwd.hip", "fa_fwd_f16.hip", "fa_bwd_dkdv.hip", "fa_bwd_dq.hip", "fa_bwd_f16.hip",
            "fa_bwd_split.hip", "fa_probe.hip", "fa_api.hip"]
 
@@ -62,7 +68,7 @@ def _scratch_kernels(remarks: str):
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj,
+    cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj,
            "-Rpass-analysis=kernel-resource-usage"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

@@ -262,6 +262,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  // K and V live in accumulator registers (see dkdv_pipe_d128).
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    asm("" : "+a"(kf[ks]));
+    asm("" : "+a"(vf[ks]));
+  }
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -505,6 +511,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
       kf[ks] = *reinterpret_cast<const V8<T>*>(krow + ks * 16 + g * 8);
       vf[ks] = *reinterpret_cast<const V8<T>*>(vrow + ks * 16 + g * 8);
     }
+    // K and V stay in accumulator registers for the whole kernel: MFMAs read
+    // their A and B operands from either file, so these 64 registers cost no
+    // copies, and the architectural file keeps room for the S and dP products
+    // and the dK and dV sums (this file is built with the VGPR accumulator
+    // form of the MFMAs, so S and dP reach the softmax-gradient arithmetic
+    // without a v_accvgpr_read per element).
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      asm("" : "+a"(kf[ks]));
+      asm("" : "+a"(vf[ks]));
+    }
   }
   if (ntiles > 0) {
     store_rows(0);
@@ -605,7 +622,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
         for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(nq, nr, ks * 2);
       }
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) dp = Mfma<T>::mma(of[ks], vf[ks], dp);
+      for (int ks = 0; ks < 8; ++ks) {
+        asm("" : "+a"(of[ks]));  // dO rows are read into accumulator registers
+        dp = Mfma<T>::mma(of[ks], vf[ks], dp);
+      }
 #pragma unroll
       for (int r = 8; r < 16; ++r) {
         p[r] = fast_exp2(__builtin_fmaf(s[r], cs, -sel(l4, r)));
