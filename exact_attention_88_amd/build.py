@@ -26,12 +26,14 @@ FLAGS = [
     "-Wno-unused-result", "-ffp-contract=fast",
     "-I", os.path.join(ROOT, "include"),
 ]
-# Per-file flags.  fa_bwd_f16.hip: every MFMA takes the form whose accumulator
-# (C and D) is in architectural VGPRs, also in its one-wave-per-SIMD dK/dV
-# kernels, whose 512-register budget would otherwise put every product in
-# accumulator registers and read each score and dP element back with a
-# v_accvgpr_read; those kernels keep K and V in accumulator registers instead.
-EXTRA_FLAGS = {"fa_bwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-file flags.  The backward files: every MFMA takes the form whose
+# accumulator (C and D) is in architectural VGPRs, also in their
+# one-wave-per-SIMD kernels, whose 512-register budget would otherwise put
+# every product in accumulator registers and read each score and dP element
+# back with a v_accvgpr_read; those kernels keep MFMA operands (K, V, dO rows)
+# in accumulator registers instead.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA_FLAGS = {"fa_bwd_f16.hip": _VGPR_FORM, "fa_bwd_dkdv.hip": _VGPR_FORM, "fa_bwd_dq.hip": _VGPR_FORM}
 SOURCES = ["fa_fwd.hip", "fa_fwd_f16.hip", "fa_bwd_dkdv.hip", "fa_bwd_dq.hip", "fa_bwd_f16.hip",
            "fa_bwd_split.hip", "fa_probe.hip", "fa_api.hip"]
 
@@ -45,12 +47,12 @@ def hipcc() -> str:
 
 # Any kernel that uses scratch (spilled or stack-allocated) memory is a build
 # error: spilling tile configurations are pruned from the tile tables.  The
-# exceptions are the generic fp32 head-dim-128 backward kernels, where every
-# candidate spills and the one that spills least is kept (mangled-name
-# fragments of the allowed instantiations: the non-causal dK/dV kernel, and
-# the dQ kernel; the causal dK/dV kernel, which accumulates dK and dV in two
-# passes of two column blocks each, no longer spills).
-ALLOWED_SCRATCH = ("11dkdv_kernelIfLi128ELi32ELi4ELi1ELb0E", "9dq_kernelIfLi128ELi32ELi4ELi1E")
+# one exception is the generic fp32 head-dim-128 non-causal dK/dV kernel
+# (92 bytes per lane with VGPR-form MFMAs and K, V in accumulator registers;
+# the only candidate whose LDS fits), kept so that the shape has a kernel; a
+# four-pass version that does not spill ran 63 % slower.  (Mangled-name
+# fragment of the allowed instantiation.)
+ALLOWED_SCRATCH = ("11dkdv_kernelIfLi128ELi32ELi4ELi1ELb0E",)
 
 
 def _scratch_kernels(remarks: str):

@@ -161,6 +161,17 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
   typename M::frag kf[NKS], vf[NKS];
   load_row_frags<T, D>(kf, kbase, a.k.ss, a.k.sd, kj, a.Sk, a.vec & VEC_K);
   load_row_frags<T, D>(vf, vbase, a.v.ss, a.v.sd, kj, a.Sk, a.vec & VEC_V);
+  if constexpr (NPASS == 2) {
+    // fp32 at head dim 128: K and V (128 registers) stay in accumulator
+    // registers as MFMA operands (this file is built with the VGPR
+    // accumulator form), leaving the architectural file to the scores and
+    // the dK, dV sums.
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      asm("" : "+a"(kf[ks]));
+      asm("" : "+a"(vf[ks]));
+    }
+  }
 
   f32x16 dk[NDB], dv[NDB];
   const float cs = a.scale_log2;
