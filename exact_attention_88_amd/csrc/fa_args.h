@@ -58,10 +58,13 @@ const TileCfg* fwd_tile(int dtype, int D, int id);
 int fwd_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s);
 
-// Tuned 16-bit (fp16 and bf16) head-dim-128 forward (fa_fwd_f16.hip).
-int fwd_fast_variants();
-TileCfg fwd_fast_cfg(int variant);
-hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int dtype, int causal, hipStream_t s);
+// Tuned 16-bit (fp16 and bf16) forward for head dims 128 and 64
+// (fa_fwd_f16.hip); fwd_fast_runs tells whether launch_fwd_fast can take
+// these arguments (else a generic entry runs).
+int fwd_fast_variants(int D);
+TileCfg fwd_fast_cfg(int variant, int D);
+bool fwd_fast_runs(const FwdArgs& a, int dtype, int D);
+hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int dtype, int D, int causal, hipStream_t s);
 
 int dkdv_tile_count(int dtype, int D);
 const TileCfg* dkdv_tile(int dtype, int D, int id);

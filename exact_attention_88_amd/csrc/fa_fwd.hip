@@ -251,9 +251,9 @@ constexpr int count_for(int dt, int D) { return count_ok(dt, D); }
 
 }  // namespace
 
-// fp16 with head dim 128 puts the tuned kernel's variants (fa_fwd_f16.hip)
-// first in its table; the generic entries follow.
-static int fast_count(int dtype, int D) { return (table_dt(dtype) == 0 && D == 128) ? fwd_fast_variants() : 0; }
+// 16-bit types with head dim 128 or 64 put the tuned kernel's variants
+// (fa_fwd_f16.hip) first in their tables; the generic entries follow.
+static int fast_count(int dtype, int D) { return table_dt(dtype) == 0 ? fwd_fast_variants(D) : 0; }
 
 static int generic_count(int dtype, int D) {
   switch (D) {
@@ -282,7 +282,7 @@ const TileCfg* fwd_tile(int dtype, int D, int id) {
   if (id < 0 || id >= fwd_tile_count(dtype, D)) return nullptr;
   const int nf = fast_count(dtype, D);
   if (id < nf) {
-    cfg = fwd_fast_cfg(id);
+    cfg = fwd_fast_cfg(id, D);
     return &cfg;
   }
   const int raw = raw_for(dtype, D, id - nf);
@@ -305,10 +305,12 @@ int fwd_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s) {
   const int nf = fast_count(dtype, D);
   if (tile < nf) {
-    // The tuned kernel needs 16-byte vector access to q, k, v and out; other
-    // layouts run the generic kernel's first entry instead.
+    // The tuned kernel needs 16-byte vector access to q, k, v and out (and,
+    // at D = 64, 31-bit row offsets); other arguments run the generic
+    // kernel's first entry instead.
     const int need = VEC_Q | VEC_K | VEC_V | VEC_O;
-    if ((a.vec & need) == need) return launch_fwd_fast(a, tile, dtype, causal, s);
+    if ((a.vec & need) == need && fwd_fast_runs(a, dtype, D))
+      return launch_fwd_fast(a, tile, dtype, D, causal, s);
     tile = nf;
   }
   const int raw = raw_for(dtype, D, tile - nf);

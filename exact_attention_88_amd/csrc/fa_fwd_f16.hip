@@ -510,14 +510,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_f16_d128_pipe(FwdArgs a) {
 //     and V(t+1) and frees the buffers of K(t+1) and V(t), which are refilled
 //     with K(t+3) and V(t+2) right after it.
 // Needs 31-bit byte offsets for every K and V row below Sk + 4*64 and a row
-// stride of at least 128 elements (checked on the host).
+// stride of at least D elements (checked on the host).
 // NW waves of 32 query rows (8, or 4 so that two workgroups share a CU and
 // one's prologue and epilogue overlap the other's tiles; either way two
 // waves per SIMD).
-template <class T, bool CAUSAL, int NW = 8>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_dma_d128(FwdArgs a) {
+// Head dim D = 128 or 64.  At D = 64 a tile holds half the MFMAs (QK^T takes
+// four k-steps, O two column blocks) for the same softmax work, so each of
+// the four regions interleaves four MFMAs with twice the VALU per MFMA.
+template <class T, bool CAUSAL, int NW = 8, int D = 128>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_dma(FwdArgs a) {
   static_assert(NW == 4 || NW == 8, "buffer loads move whole multiples of 16 rows");
-  constexpr int BM = 32 * NW, BN = 64, TR = BN * kD;
+  static_assert(D == 128 || D == 64, "tuned head dims");
+  constexpr int BM = 32 * NW, BN = 64, TR = BN * D;
+  constexpr int NK = D / 16;  // k-steps of QK^T (and K fragments per 32 keys)
+  constexpr int ND = D / 32;  // 32-column blocks of O
+  // Per scheduling group (one MFMA each): exponentials of regions 1 and 2/3,
+  // other VALU.
+  constexpr int kTr1 = 16 / NK, kTr2 = 8 / NK, kVa = 24 / NK;
   __shared__ __attribute__((aligned(1024))) T smem[4 * TR];  // K0 K1 V0 V1
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, c = lane & 31;
@@ -534,19 +543,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dma_d128(FwdArgs a) {
 
   const int q0 = qb * BM, qi = q0 + w * 32 + c;
 
-  V8<T> qf[8];
+  V8<T> qf[NK];
   {
     const T* qrow = qbase + (int64_t)min(qi, a.Sq - 1) * a.q.ss;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const V8<T>*>(qrow + ks * 16 + g * 8);
+    for (int ks = 0; ks < NK; ++ks) qf[ks] = *reinterpret_cast<const V8<T>*>(qrow + ks * 16 + g * 8);
   }
   // Q resident before any buffer load into LDS is issued (the compiler does
   // not count those).
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-  f32x16 oacc[4];
+  f32x16 oacc[ND];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) oacc[i] = zero16();
+  for (int i = 0; i < ND; ++i) oacc[i] = zero16();
   float m = -INFINITY, lsum = 0.f, mc = 0.f;
   const float cs = a.scale_log2;
 
@@ -563,12 +572,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dma_d128(FwdArgs a) {
   auto vbuf = [&](int par) { return smem + 2 * TR + (par & 1) * TR; };
   const unsigned lds0 = swzl::lds_addr(smem);
   const int ksb = (int)(a.k.ss * (int64_t)sizeof(T)), vsb = (int)(a.v.ss * (int64_t)sizeof(T));
-  const int klo = swzl::dma_lane_off<NW>(ksb), vlo = swzl::dma_lane_off<NW>(vsb);
+  const int klo = swzl::dma_lane_off<NW, D>(ksb), vlo = swzl::dma_lane_off<NW, D>(vsb);
   auto dma_k = [&](int t, int par) {
-    swzl::tile_dma<BN, NW>(rk, lds0 + (unsigned)((par & 1) * TR * (int)sizeof(T)), klo, ksb, t * BN);
+    swzl::tile_dma<BN, NW, D>(rk, lds0 + (unsigned)((par & 1) * TR * (int)sizeof(T)), klo, ksb, t * BN);
   };
   auto dma_v = [&](int t, int par) {
-    swzl::tile_dma<BN, NW>(rv, lds0 + (unsigned)((2 + (par & 1)) * TR * (int)sizeof(T)), vlo, vsb, t * BN);
+    swzl::tile_dma<BN, NW, D>(rv, lds0 + (unsigned)((2 + (par & 1)) * TR * (int)sizeof(T)), vlo, vsb, t * BN);
+  };
+  auto kfrag = [](const T* buf, int rbase, int kchunk) { return swzl::frag_r_swz<T, D>(buf, rbase, kchunk); };
+  auto vfrag = [](const T* buf, int rbase, int tt, int cbase) {
+    return swzl::frag_t_swz<T, D>(buf, rbase, tt, cbase);
   };
   auto barrier = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's buffer loads are in LDS
@@ -606,7 +619,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dma_d128(FwdArgs a) {
       const float alpha = raise ? fast_exp2((m - mnew) * cs) : 1.f;
       lsum *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
@@ -619,7 +632,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dma_d128(FwdArgs a) {
   };
 
   f32x16 sa[2], sb[2];
-  V8<T> kf[8];
+  V8<T> kf[NK];
   if (ntiles > 0) {
     dma_k(0, 0);
     dma_k(1, 1);
@@ -628,16 +641,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dma_d128(FwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(kbuf(0), kb * 32, ks * 2);
+      for (int ks = 0; ks < NK; ++ks) kf[ks] = kfrag(kbuf(0), kb * 32, ks * 2);
       sa[kb] = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) sa[kb] = Mfma<T>::mma(kf[ks], qf[ks], sa[kb]);
+      for (int ks = 0; ks < NK; ++ks) sa[kb] = Mfma<T>::mma(kf[ks], qf[ks], sa[kb]);
     }
     __syncthreads();  // every wave has read K(0)'s buffer
     dma_k(2, 0);
     dma_v(1, 1);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(kbuf(1), 0, ks * 2);
+    for (int ks = 0; ks < NK; ++ks) kf[ks] = kfrag(kbuf(1), 0, ks * 2);
     rowmax(sa, 0);
   }
 
@@ -654,67 +667,67 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dma_d128(FwdArgs a) {
     constexpr int P = decltype(parity)::value;  // t & 1
     const T* Kn = kbuf(P + 1);
     const T* Vc = vbuf(P);
-    V8<T> vt[2][4], pf[2][2];
+    V8<T> vt[2][ND], pf[2][2];
     float rs = 0.f;
     // ---- 1
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) vt[tt][db] = swzl::frag_t_swz(Vc, 0, tt, db * 32);
+      for (int db = 0; db < ND; ++db) vt[tt][db] = vfrag(Vc, 0, tt, db * 32);
     sn[0] = zero16();
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) sn[0] = Mfma<T>::mma(kf[ks], qf[ks], sn[0]);
+    for (int ks = 0; ks < NK; ++ks) sn[0] = Mfma<T>::mma(kf[ks], qf[ks], sn[0]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[0][r] = fast_exp2(__builtin_fmaf(sc[0][r], cs, -mc));
     pf[0][0] = frag_from_acc<T>(sc[0], 0);
     pf[0][1] = frag_from_acc<T>(sc[0], 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, kTr1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- 2
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(Kn, 32, ks * 2);
+    for (int ks = 0; ks < NK; ++ks) kf[ks] = kfrag(Kn, 32, ks * 2);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] = Mfma<T>::mma(vt[tt][db], pf[0][tt], oacc[db]);
+      for (int db = 0; db < ND; ++db) oacc[db] = Mfma<T>::mma(vt[tt][db], pf[0][tt], oacc[db]);
 #pragma unroll
     for (int r = 0; r < 8; ++r) sc[1][r] = fast_exp2(__builtin_fmaf(sc[1][r], cs, -mc));
     pf[1][0] = frag_from_acc<T>(sc[1], 0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) rs += sc[0][r];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, kTr2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- 3
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) vt[tt][db] = swzl::frag_t_swz(Vc, 32, tt, db * 32);
+      for (int db = 0; db < ND; ++db) vt[tt][db] = vfrag(Vc, 32, tt, db * 32);
     sn[1] = zero16();
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) sn[1] = Mfma<T>::mma(kf[ks], qf[ks], sn[1]);
+    for (int ks = 0; ks < NK; ++ks) sn[1] = Mfma<T>::mma(kf[ks], qf[ks], sn[1]);
 #pragma unroll
     for (int r = 8; r < 16; ++r) sc[1][r] = fast_exp2(__builtin_fmaf(sc[1][r], cs, -mc));
     pf[1][1] = frag_from_acc<T>(sc[1], 1);
 #pragma unroll
     for (int r = 0; r < 16; ++r) rs += sc[1][r];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, kTr2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // Publish K(t+2) and V(t+1); the buffers of K(t+1) and V(t) are free.
@@ -723,11 +736,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dma_d128(FwdArgs a) {
     dma_v(t + 2, P);
     // ---- 4
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kf[ks] = swzl::frag_r_swz(kbuf(P), 0, ks * 2);
+    for (int ks = 0; ks < NK; ++ks) kf[ks] = kfrag(kbuf(P), 0, ks * 2);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] = Mfma<T>::mma(vt[tt][db], pf[1][tt], oacc[db]);
+      for (int db = 0; db < ND; ++db) oacc[db] = Mfma<T>::mma(vt[tt][db], pf[1][tt], oacc[db]);
     lsum += rs;
     __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < ntiles) rowmax(sn, t + 1);
@@ -749,7 +762,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dma_d128(FwdArgs a) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;  // no visible key: O = 0, LSE = -inf
     T* orow = (T*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qi * a.o.ss;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         V4<T> o4;
@@ -787,48 +800,77 @@ hipError_t launch_plain(const FwdArgs& a, int causal, hipStream_t s) {
 // Byte offsets of every K and V row the buffer-load kernel may address fit in
 // 31 bits, and rows do not overlap.  The last loads reach K tile ntiles + 2,
 // whose rows end below Sk + 4*64.
-bool fwd_dma_fits(const FwdArgs& a, int esize) {
+bool fwd_dma_fits(const FwdArgs& a, int esize, int D) {
   const int64_t lim = (int64_t)1 << 31;
-  return a.k.ss >= kD && a.v.ss >= kD && ((int64_t)a.Sk + 4 * 64) * a.k.ss * esize < lim &&
+  return a.k.ss >= D && a.v.ss >= D && ((int64_t)a.Sk + 4 * 64) * a.k.ss * esize < lim &&
          ((int64_t)a.Sk + 4 * 64) * a.v.ss * esize < lim;
 }
 
 template <class T>
 hipError_t launch_variant(const FwdArgs& a, int variant, int causal, hipStream_t s) {
+  const bool fits = fwd_dma_fits(a, (int)sizeof(T), kD);
   switch (variant) {
     case 0: return launch_pipe<T, 64, 8, true>(a, causal, s);
     case 1: return launch_pipe<T, 64, 8, false>(a, causal, s);
     case 2: return launch_plain<T, 64, 8>(a, causal, s);
     case 3: return launch_plain<T, 64, 4>(a, causal, s);
     case 4:
-      if (!fwd_dma_fits(a, (int)sizeof(T))) return launch_pipe<T, 64, 8, true>(a, causal, s);
-      return causal ? launch_k(&fwd_dma_d128<T, true>, 256, 512, a, s)
-                    : launch_k(&fwd_dma_d128<T, false>, 256, 512, a, s);
+      if (!fits) return launch_pipe<T, 64, 8, true>(a, causal, s);
+      return causal ? launch_k(&fwd_dma<T, true>, 256, 512, a, s)
+                    : launch_k(&fwd_dma<T, false>, 256, 512, a, s);
     case 5:
-      if (!fwd_dma_fits(a, (int)sizeof(T))) return launch_plain<T, 64, 4>(a, causal, s);
-      return causal ? launch_k(&fwd_dma_d128<T, true, 4>, 128, 256, a, s)
-                    : launch_k(&fwd_dma_d128<T, false, 4>, 128, 256, a, s);
+      if (!fits) return launch_plain<T, 64, 4>(a, causal, s);
+      return causal ? launch_k(&fwd_dma<T, true, 4>, 128, 256, a, s)
+                    : launch_k(&fwd_dma<T, false, 4>, 128, 256, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class T>
+hipError_t launch_variant64(const FwdArgs& a, int variant, int causal, hipStream_t s) {
+  switch (variant) {
+    case 0:
+      return causal ? launch_k(&fwd_dma<T, true, 8, 64>, 256, 512, a, s)
+                    : launch_k(&fwd_dma<T, false, 8, 64>, 256, 512, a, s);
+    case 1:
+      return causal ? launch_k(&fwd_dma<T, true, 4, 64>, 128, 256, a, s)
+                    : launch_k(&fwd_dma<T, false, 4, 64>, 128, 256, a, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Variants (BN keys per tile, waves): pipelined 0 = (64, 8, ordered),
-// 1 = (64, 8); plain 2 = (64, 8), 3 = (64, 4); 4 = pipelined (64, 8) with
-// buffer loads into LDS (variant 0 runs instead where its 31-bit offsets do
-// not reach every row); 5 = variant 4 with 4 waves, 128 query rows per
-// workgroup and two workgroups per CU (variant 3 runs instead where the
+// Head dim 128 variants (BN keys per tile, waves): pipelined 0 = (64, 8,
+// ordered), 1 = (64, 8); plain 2 = (64, 8), 3 = (64, 4); 4 = pipelined
+// (64, 8) with buffer loads into LDS (variant 0 runs instead where its 31-bit
+// offsets do not reach every row); 5 = variant 4 with 4 waves, 128 query rows
+// per workgroup and two workgroups per CU (variant 3 runs instead where the
 // offsets do not reach).
-int fwd_fast_variants() { return 6; }
+// Head dim 64: the buffer-load kernel with 8 (variant 0) or 4 (variant 1)
+// waves; where its offsets do not reach, the caller runs a generic entry.
+int fwd_fast_variants(int D) { return D == 128 ? 6 : D == 64 ? 2 : 0; }
 
-TileCfg fwd_fast_cfg(int v) {
+TileCfg fwd_fast_cfg(int v, int D) {
+  if (D == 64) {
+    const int nw = v == 1 ? 4 : 8;
+    return TileCfg{32 * nw, 64, nw, 4 * 64 * 64 * 2};
+  }
   const int nw = v == 3 || v == 5 ? 4 : 8;
   if (v >= 4) return TileCfg{32 * nw, 64, nw, 4 * 64 * kD * 2};
   return TileCfg{32 * nw, 64, nw, 2 * 64 * (kLSK + kLSV) * 2};
 }
 
-hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int dtype, int causal, hipStream_t s) {
+bool fwd_fast_runs(const FwdArgs& a, int dtype, int D) {
+  (void)dtype;
+  return D == 128 || fwd_dma_fits(a, 2, D);
+}
+
+hipError_t launch_fwd_fast(const FwdArgs& a, int variant, int dtype, int D, int causal, hipStream_t s) {
+  if (D == 64) {
+    if (dtype == 2) return launch_variant64<bf16_t>(a, variant, causal, s);
+    return launch_variant64<half_t>(a, variant, causal, s);
+  }
   if (dtype == 2) return launch_variant<bf16_t>(a, variant, causal, s);
   return launch_variant<half_t>(a, variant, causal, s);
 }

@@ -1,11 +1,11 @@
-// LDS tile layout and global -> LDS loads shared by the tuned 16-bit
-// head-dim-128 kernels (fa_fwd_f16.hip, fa_bwd_f16.hip).
+// LDS tile layout and global -> LDS loads shared by the tuned 16-bit kernels
+// (fa_fwd_f16.hip, fa_bwd_f16.hip, fa_bwd_split.hip).
 //
-// Tiles are rows of 128 16-bit elements (256 bytes) stored unpadded in an
-// XOR-swizzled layout that one copy serves for both row-wise MFMA operand
-// reads (ds_read_b128) and transposed ones (ds_read_b64_tr_b16), and are
-// filled either through registers or straight from global memory with buffer
-// loads that write LDS.
+// Tiles are rows of D 16-bit elements (D = 128: 256 bytes, D = 64: 128
+// bytes) stored unpadded in an XOR-swizzled layout that one copy serves for
+// both row-wise MFMA operand reads (ds_read_b128) and transposed ones
+// (ds_read_b64_tr_b16), and are filled either through registers or straight
+// from global memory with buffer loads that write LDS.
 #pragma once
 
 #include "fa_common.h"
@@ -13,15 +13,28 @@
 namespace fa {
 namespace swzl {
 
-constexpr int kD = 128;  // elements per tile row
+constexpr int kD = 128;  // default elements per tile row
 
-// Single-copy swizzled layout: unpadded 256-byte rows in which the 16-byte
-// chunk k of row r sits at chunk position k ^ swz(r).  swz(r) takes distinct
-// values on any 16 consecutive rows (so 16-row ds_read_b128 row reads and
-// full-row stores are conflict free) and, on 4 rows that start at a multiple
-// of 4, spreads 4 neighbouring chunks over all 16 chunk positions (so 4-row
-// transposed reads are conflict free).  One layout serves both read patterns.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Single-copy swizzled layout: unpadded rows in which the 16-byte chunk k of
+// row r sits at chunk position k ^ swz<D>(r).  LDS serves 64 four-byte banks,
+// i.e. 16 chunk positions per 256 bytes.
+//   D = 128 (16 chunks a row): swz(r) takes distinct values on any 16
+//   consecutive rows (16-row ds_read_b128 reads of one chunk and full-row
+//   stores are conflict free) and, on 4 rows that start at a multiple of 4,
+//   spreads 4 neighbouring chunks over all 16 chunk positions (4-row
+//   transposed reads are conflict free).
+//   D = 64 (8 chunks, two rows per 256 bytes): the row's parity picks the
+//   bank half, and swz(r) in 0..7 is distinct over the 8 even and over the 8
+//   odd rows of any 16 aligned rows (row reads) and differs in bit 2 between
+//   rows 4i and 4i+2 (and 4i+1, 4i+3), so 4 aligned rows x 4 neighbouring
+//   chunks (a transposed read) cover all 16 positions.
+// Either way swz has period 16 in r.
+template <int D = kD>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 128 || D == 64, "tuned tiles are 64 or 128 elements wide");
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 template <int ROWS, int NT, class T>
 __device__ __forceinline__ void tile_store_swz(const u32x4* r, T* lds) {
@@ -33,24 +46,24 @@ __device__ __forceinline__ void tile_store_swz(const u32x4* r, T* lds) {
 }
 
 // Row-wise fragment in the swizzled layout; rbase is a multiple of 16.
-template <class T>
+template <class T, int D = kD>
 __device__ __forceinline__ V8<T> frag_r_swz(const T* lds, int rbase, int kchunk) {
   const int lane = threadIdx.x & 63, r = lane & 31;
-  return *reinterpret_cast<const V8<T>*>(lds + (rbase + r) * kD +
-                                      (((kchunk + (lane >> 5)) ^ swz(r)) << 3));
+  return *reinterpret_cast<const V8<T>*>(lds + (rbase + r) * D +
+                                      (((kchunk + (lane >> 5)) ^ swz<D>(r)) << 3));
 }
 
 // Transposed fragment in the swizzled layout (same lanes as frag_t); rbase is
 // a multiple of 16 and cbase of 8.
-template <class T>
+template <class T, int D = kD>
 __device__ __forceinline__ V8<T> frag_t_swz(const T* lds, int rbase, int t, int cbase) {
   const int lane = threadIdx.x & 63, g = lane >> 5, j = lane & 15;
   const int col = ((lane >> 4) & 1) * 16 + (j & 3) * 4;
   const int r = g * 4 + (j >> 2);
   const int ch = (cbase >> 3) + (col >> 3);
   typedef __attribute__((address_space(3))) s4 lds_s4;
-  const T* p0 = lds + (rbase + t * 16 + r) * kD + ((ch ^ swz(r)) << 3) + (col & 7);
-  const T* p1 = lds + (rbase + t * 16 + r + 8) * kD + ((ch ^ swz(r + 8)) << 3) + (col & 7);
+  const T* p0 = lds + (rbase + t * 16 + r) * D + ((ch ^ swz<D>(r)) << 3) + (col & 7);
+  const T* p1 = lds + (rbase + t * 16 + r + 8) * D + ((ch ^ swz<D>(r + 8)) << 3) + (col & 7);
   s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
   s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1));
   V4<T> ah = __builtin_bit_cast(V4<T>, a), bh = __builtin_bit_cast(V4<T>, b);
@@ -90,35 +103,38 @@ __device__ __forceinline__ void dma16(rsrc_t r, unsigned m0, int voff) {
                :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
 }
 
-// Rows of 16-bit elements, 256 bytes each, in LDS.
-constexpr int kRowBytes = kD * 2;
-
-// tile_dma moves ROWS rows x 256 bytes into the swizzled layout with
-// ROWS/(4*NW) wave-wide 1 KB loads (4 rows each) shared by the NW waves: load
-// i of wave w covers tile rows (i*NW + w)*4 .. +3; lane l takes row
-// (i*NW + w)*4 + l/16, fetches that row's 16-byte chunk (l%16) ^ swz(row) and
-// writes it at chunk position l%16 (so chunk k sits at position k ^ swz(row)).
-// With NW a multiple of 4 every load moves the rows by a multiple of 16,
-// which leaves swz(row) unchanged, so a lane's global byte offset is a
+// tile_dma moves ROWS rows of D 16-bit elements into the swizzled layout with
+// wave-wide 1 KB loads shared by the NW waves, each covering RL = 1024 / (2D)
+// rows (D = 128: 4 rows of 16 chunks, D = 64: 8 rows of 8 chunks): load i of
+// wave w covers tile rows (i*NW + w)*RL .. +RL-1; lane l takes row
+// (i*NW + w)*RL + l/C (C = D/8 chunks a row), fetches that row's 16-byte chunk
+// (l%C) ^ swz(row) and writes it at chunk position l%C (so chunk k sits at
+// position k ^ swz(row)).  When NW*RL is a multiple of 16 every load moves the
+// rows by a multiple of swz's period, so a lane's global byte offset is a
 // per-lane part fixed for the kernel (dma_lane_off, for row stride ss_bytes)
 // plus a wave-uniform row offset: one vector add per load.
-template <int NW>
+template <int D>
+constexpr int dma_rows() { return 1024 / (2 * D); }
+
+template <int NW, int D = kD>
 __device__ __forceinline__ int dma_lane_off(int ss_bytes) {
-  static_assert(NW % 4 == 0, "loads move whole multiples of 16 rows");
-  const int lane = threadIdx.x & 63, row = ((int)threadIdx.x >> 6) * 4 + (lane >> 4);
-  return row * ss_bytes + (((lane & 15) ^ swz(row)) << 4);
+  constexpr int RL = dma_rows<D>(), C = D / 8;
+  static_assert((NW * RL) % 16 == 0, "loads move whole multiples of 16 rows");
+  const int lane = threadIdx.x & 63, row = ((int)threadIdx.x >> 6) * RL + lane / C;
+  return row * ss_bytes + (((lane % C) ^ swz<D>(row)) << 4);
 }
 
 // ROWS rows starting at global row row0 into the tile at LDS byte address lds
 // (wave-uniform).  The caller guarantees that every byte offset fits in 31
 // bits; rows past the buffer's byte range read as zero.
-template <int ROWS, int NW>
+template <int ROWS, int NW, int D = kD>
 __device__ __forceinline__ void tile_dma(rsrc_t r, unsigned lds, int lane_off, int ss_bytes, int row0) {
-  static_assert(ROWS % (4 * NW) == 0 && NW % 4 == 0, "whole wave loads of 16-row multiples");
+  constexpr int RL = dma_rows<D>();
+  static_assert(ROWS % (RL * NW) == 0 && (NW * RL) % 16 == 0, "whole wave loads of 16-row multiples");
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 #pragma unroll
-  for (int i = 0; i < ROWS / (4 * NW); ++i)
-    dma16(r, lds + (unsigned)((i * NW + w) * 4 * kRowBytes), lane_off + (row0 + i * NW * 4) * ss_bytes);
+  for (int i = 0; i < ROWS / (RL * NW); ++i)
+    dma16(r, lds + (unsigned)((i * NW + w) * 1024), lane_off + (row0 + i * NW * RL) * ss_bytes);
 }
 
 }  // namespace swzl
