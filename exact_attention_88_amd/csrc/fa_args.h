@@ -86,14 +86,18 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int D, hipStream_t s);
 int probe_workgroups();
 hipError_t launch_probe(int kind, int iters, float* sink, hipStream_t s);
 
-// Tuned fp16 / head-dim-128 backward kernels (fa_bwd_f16.hip).
-int dq_fast_variants();
-TileCfg dq_fast_cfg(int variant);
-hipError_t launch_dq_fast(const BwdArgs& a, int variant, int dtype, int causal, hipStream_t s);
-bool dq_fast_fuses_delta(const BwdArgs& a, int variant, int dtype);
-int dkdv_fast_variants();
-TileCfg dkdv_fast_cfg(int variant);
-hipError_t launch_dkdv_fast(const BwdArgs& a, int variant, int dtype, int causal, hipStream_t s);
+// Tuned 16-bit (fp16, bf16) backward kernels for head dims 128 and 64
+// (fa_bwd_f16.hip); *_fast_runs tells whether the launcher can take these
+// arguments (else a generic entry runs).
+int dq_fast_variants(int D);
+TileCfg dq_fast_cfg(int variant, int D);
+bool dq_fast_runs(const BwdArgs& a, int dtype, int D);
+hipError_t launch_dq_fast(const BwdArgs& a, int variant, int dtype, int D, int causal, hipStream_t s);
+bool dq_fast_fuses_delta(const BwdArgs& a, int variant, int dtype, int D);
+int dkdv_fast_variants(int D);
+TileCfg dkdv_fast_cfg(int variant, int D);
+bool dkdv_fast_runs(const BwdArgs& a, int dtype, int D);
+hipError_t launch_dkdv_fast(const BwdArgs& a, int variant, int dtype, int D, int causal, hipStream_t s);
 // dK/dV with each 32-key slice split over a score wave and an accumulate wave
 // (fa_bwd_split.hip).
 bool dkdv_split_fits(const BwdArgs& a, int esize);

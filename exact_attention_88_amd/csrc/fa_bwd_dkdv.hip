@@ -357,9 +357,9 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// fp16 with head dim 128 puts the tuned kernel's variants (fa_bwd_f16.hip)
-// first in its table; the generic entries follow.
-static int fast_count(int dtype, int D) { return (table_dt(dtype) == 0 && D == 128) ? dkdv_fast_variants() : 0; }
+// 16-bit types with head dim 128 or 64 put the tuned kernel's variants
+// (fa_bwd_f16.hip) first in their tables; the generic entries follow.
+static int fast_count(int dtype, int D) { return table_dt(dtype) == 0 ? dkdv_fast_variants(D) : 0; }
 
 static int generic_count(int dtype, int D) {
   switch (D) {
@@ -378,7 +378,7 @@ const TileCfg* dkdv_tile(int dtype, int D, int id) {
   if (id < 0 || id >= dkdv_tile_count(dtype, D)) return nullptr;
   const int nf = fast_count(dtype, D);
   if (id < nf) {
-    cfg = dkdv_fast_cfg(id);
+    cfg = dkdv_fast_cfg(id, D);
     return &cfg;
   }
   id -= nf;
@@ -399,10 +399,12 @@ int dkdv_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
 hipError_t launch_dkdv(const BwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s) {
   const int nf = fast_count(dtype, D);
   if (tile < nf) {
-    // The tuned kernel needs 16-byte vector access to every tensor it touches;
-    // other layouts run the generic kernel's first entry instead.
+    // The tuned kernel needs 16-byte vector access to every tensor it touches
+    // (and, at D = 64, 31-bit row offsets); other arguments run the generic
+    // kernel's first entry instead.
     const int need = VEC_Q | VEC_K | VEC_V | VEC_DO | VEC_DK | VEC_DV;
-    if ((a.vec & need) == need) return launch_dkdv_fast(a, tile, dtype, causal, s);
+    if ((a.vec & need) == need && dkdv_fast_runs(a, dtype, D))
+      return launch_dkdv_fast(a, tile, dtype, D, causal, s);
     tile = nf;
   }
   const int raw = raw_for(dtype, D, tile - nf);

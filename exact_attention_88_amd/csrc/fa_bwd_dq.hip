@@ -233,9 +233,9 @@ int raw_for(int dtype, int D, int id) {
 
 }  // namespace
 
-// fp16 with head dim 128 puts the tuned kernel's variants (fa_bwd_f16.hip)
-// first in its table; the generic entries follow.
-static int fast_count(int dtype, int D) { return (table_dt(dtype) == 0 && D == 128) ? dq_fast_variants() : 0; }
+// 16-bit types with head dim 128 or 64 put the tuned kernel's variants
+// (fa_bwd_f16.hip) first in their tables; the generic entries follow.
+static int fast_count(int dtype, int D) { return table_dt(dtype) == 0 ? dq_fast_variants(D) : 0; }
 
 static int generic_count(int dtype, int D) {
   switch (D) {
@@ -254,7 +254,7 @@ const TileCfg* dq_tile(int dtype, int D, int id) {
   if (id < 0 || id >= dq_tile_count(dtype, D)) return nullptr;
   const int nf = fast_count(dtype, D);
   if (id < nf) {
-    cfg = dq_fast_cfg(id);
+    cfg = dq_fast_cfg(id, D);
     return &cfg;
   }
   id -= nf;
@@ -269,22 +269,27 @@ int dq_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
   // swizzled single-copy layout and buffer loads into LDS measured fastest on
   // MI355X at S = 4096 and 16384, causal and not.
   if (table_dt(dtype) == 0 && D == 128) return 5;
+  // 16-bit, D = 64: the buffer-load kernel with 4 waves, fastest at every
+  // length from 128 to 16384.
+  if (table_dt(dtype) == 0 && D == 64) return 1;
   return 0;
 }
 
 bool dq_can_fuse_delta(const BwdArgs& a, int dtype, int D, int tile) {
   if (tile >= fast_count(dtype, D)) return false;
   const int need = VEC_Q | VEC_K | VEC_V | VEC_DO | VEC_DQ | VEC_O;
-  return (a.vec & need) == need && dq_fast_fuses_delta(a, tile, dtype);
+  return (a.vec & need) == need && dq_fast_fuses_delta(a, tile, dtype, D);
 }
 
 hipError_t launch_dq(const BwdArgs& a, int dtype, int D, int causal, int tile, hipStream_t s) {
   const int nf = fast_count(dtype, D);
   if (tile < nf) {
-    // The tuned kernel needs 16-byte vector access to every tensor it touches;
-    // other layouts run the generic kernel's first entry instead.
+    // The tuned kernel needs 16-byte vector access to every tensor it touches
+    // (and, at D = 64, 31-bit row offsets); other arguments run the generic
+    // kernel's first entry instead.
     const int need = VEC_Q | VEC_K | VEC_V | VEC_DO | VEC_DQ;
-    if ((a.vec & need) == need) return launch_dq_fast(a, tile, dtype, causal, s);
+    if ((a.vec & need) == need && dq_fast_runs(a, dtype, D))
+      return launch_dq_fast(a, tile, dtype, D, causal, s);
     tile = nf;
   }
   const int raw = raw_for(dtype, D, tile - nf);

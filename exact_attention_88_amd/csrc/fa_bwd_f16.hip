@@ -92,10 +92,12 @@ __device__ __forceinline__ V8<T> cvt8(const f32x16& x, int t) {
   return r;
 }
 
-template <class T>
+// Row of ND*32 columns from ND accumulators (lane (c, g): column c of the
+// transposed product, rows crow(r, g)), times mul, rounded to T.
+template <class T, int ND = 4>
 __device__ __forceinline__ void store_row4x4(T* rowp, const f32x16* acc, float mul, int g) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       V4<T> v;
@@ -427,9 +429,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
 //     are never stored.
 // Needs 32-bit byte offsets: (Sq + 3*128) * row stride * 2 bytes < 2^31 for
 // Q and dO, and a row stride of at least 128 elements (checked on the host).
-template <class T, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
-  constexpr int BM = 128, NW = 4, BN = 32 * NW, NQB = BM / 32, TR = BM * kD, BUF = 2 * TR;
+template <class T, bool CAUSAL, int D = 128>
+__global__ __launch_bounds__(256, 1) void dkdv_pipe(BwdArgs a) {
+  constexpr int BM = 128, NW = 4, BN = 32 * NW, NQB = BM / 32, TR = BM * D, BUF = 2 * TR;
+  constexpr int NK = D / 16, ND = D / 32;  // k-steps of S and dP; column blocks of dK and dV
+  // Per scheduling group (one MFMA each): LDS reads of phase 1, VALU.
+  constexpr int kDs1 = (4 * ND + 8) / NK, kVa = 32 / NK;
   __shared__ __attribute__((aligned(1024))) T smem[2 * BUF];
   __shared__ __attribute__((aligned(16))) float lsd[2][2][BM];  // [buffer][LSE*log2e, -delta][row]
 
@@ -446,9 +451,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   const float* dl = a.delta + (int64_t)bh * a.Sq;
   const int k0 = kb * BN, kw = k0 + w * 32, kj = kw + c;
 
-  f32x16 dk[4], dv[4];
+  f32x16 dk[ND], dv[ND];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { dk[i] = zero16(); dv[i] = zero16(); }
+  for (int i = 0; i < ND; ++i) { dk[i] = zero16(); dv[i] = zero16(); }
   const float cs = a.scale_log2;
 
   const int qstart = CAUSAL ? (max(0, k0 - a.coff) / BM) * BM : 0;
@@ -464,12 +469,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   bool lrow = false;
   const unsigned lds0 = lds_addr(smem);
   const int qsb = (int)(a.q.ss * (int64_t)sizeof(T)), dsb = (int)(a.dout.ss * (int64_t)sizeof(T));
-  const int qlo = dma_lane_off<NW>(qsb), dlo = dma_lane_off<NW>(dsb);
+  const int qlo = dma_lane_off<NW, D>(qsb), dlo = dma_lane_off<NW, D>(dsb);
   auto issue_tile = [&](int t, int buf) {
     const int q0 = qstart + t * BM;
     const unsigned base = lds0 + (unsigned)(buf * BUF * (int)sizeof(T));
-    tile_dma<BM, NW>(rq, base, qlo, qsb, q0);
-    tile_dma<BM, NW>(rd, base + (unsigned)(TR * (int)sizeof(T)), dlo, dsb, q0);
+    tile_dma<BM, NW, D>(rq, base, qlo, qsb, q0);
+    tile_dma<BM, NW, D>(rd, base + (unsigned)(TR * (int)sizeof(T)), dlo, dsb, q0);
     const int i = q0 + ((int)threadIdx.x & (BM - 1));
     lrow = i < a.Sq;
     lsr = lse[min(i, a.Sq - 1)];
@@ -483,9 +488,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   };
 
   // Pipeline state carried from 32-query block j-1 into block j.
-  V8<T> qf[8];         // Q rows of block j (operand of S)
-  V8<T> of[8];         // dO rows of block j (operand of dP)
-  V8<T> qtp[2][4];     // transposed Q of block j-1 (operand of dK)
+  V8<T> qf[NK];        // Q rows of block j (operand of S)
+  V8<T> of[NK];        // dO rows of block j (operand of dP)
+  V8<T> qtp[2][ND];    // transposed Q of block j-1 (operand of dK)
   f32x16 pc, dpc;      // P and dP - delta of block j-1
   V8<T> sf0;           // dS of block j-1, rows of k-step 0, rounded
   pc = zero16();
@@ -495,30 +500,30 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int db = 0; db < 4; ++db) qtp[tt][db] = sf0;
+    for (int db = 0; db < ND; ++db) qtp[tt][db] = sf0;
   // The first tile's buffer loads go out before the K and V row loads, so
   // that the prologue waits for one memory round trip, not two.  (Loads
   // issued after them complete after them, so the compiler's own waits for
   // the rows, which do not count these loads, are conservative.)
   if (ntiles > 0) issue_tile(0, 0);
-  V8<T> kf[8], vf[8];
+  V8<T> kf[NK], vf[NK];
   {
     const int kc = min(kj, a.Sk - 1);
     const T* krow = (const T*)a.k.p + b * a.k.sb + h * a.k.sh + (int64_t)kc * a.k.ss;
     const T* vrow = (const T*)a.v.p + b * a.v.sb + h * a.v.sh + (int64_t)kc * a.v.ss;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < NK; ++ks) {
       kf[ks] = *reinterpret_cast<const V8<T>*>(krow + ks * 16 + g * 8);
       vf[ks] = *reinterpret_cast<const V8<T>*>(vrow + ks * 16 + g * 8);
     }
     // K and V stay in accumulator registers for the whole kernel: MFMAs read
-    // their A and B operands from either file, so these 64 registers cost no
-    // copies, and the architectural file keeps room for the S and dP products
-    // and the dK and dV sums (this file is built with the VGPR accumulator
-    // form of the MFMAs, so S and dP reach the softmax-gradient arithmetic
-    // without a v_accvgpr_read per element).
+    // their A and B operands from either file, so these 64 (D = 128)
+    // registers cost no copies, and the architectural file keeps room for the
+    // S and dP products and the dK and dV sums (this file is built with the
+    // VGPR accumulator form of the MFMAs, so S and dP reach the
+    // softmax-gradient arithmetic without a v_accvgpr_read per element).
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < NK; ++ks) {
       asm("" : "+a"(kf[ks]));
       asm("" : "+a"(vf[ks]));
     }
@@ -529,9 +534,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
     __syncthreads();
     if (ntiles > 1) issue_tile(1, 1);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(smem, 0, ks * 2);
+    for (int ks = 0; ks < NK; ++ks) qf[ks] = frag_r_swz<T, D>(smem, 0, ks * 2);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r_swz(smem + TR, 0, ks * 2);
+    for (int ks = 0; ks < NK; ++ks) of[ks] = frag_r_swz<T, D>(smem + TR, 0, ks * 2);
   }
 
   // Rows of k-step tt of an accumulator (crow order) out of four float4 runs.
@@ -540,7 +545,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
   };
 
   // Tile t: its data is in cur, the next tile's in nxt.  Block j runs four
-  // phases, each one scheduling region whose eight MFMAs are interleaved with
+  // phases, each one scheduling region whose NK MFMAs (eight at D = 128,
+  // four at D = 64) are interleaved with
   // the LDS reads and the VALU work listed for it (a wave issues only a few
   // VALU instructions per MFMA without stalling the matrix pipe, so the
   // softmax-gradient arithmetic is spread evenly over all four):
@@ -563,14 +569,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qs = q0 + qb * 32;
-      V8<T> dt[2][4], qt[2][4], sf1, pf0, pf1;
+      V8<T> dt[2][ND], qt[2][ND], sf1, pf0, pf1;
       float4 l4[4];
       f32x16 s = zero16(), dp, p;  // dp starts from -delta: dP - delta comes out of the MFMAs
       // ---- 1
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dt[tt][db] = frag_t_swz(Dc, qb * 32, tt, db * 32);
+        for (int db = 0; db < ND; ++db) dt[tt][db] = frag_t_swz<T, D>(Dc, qb * 32, tt, db * 32);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         l4[i] = *reinterpret_cast<const float4*>(Ls + qb * 32 + i * 8 + g * 4);
@@ -578,7 +584,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
         dp[i * 4 + 0] = d.x; dp[i * 4 + 1] = d.y; dp[i * 4 + 2] = d.z; dp[i * 4 + 3] = d.w;
       }
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s = Mfma<T>::mma(qf[ks], kf[ks], s);
+      for (int ks = 0; ks < NK; ++ks) s = Mfma<T>::mma(qf[ks], kf[ks], s);
       {
         f32x16 x;
 #pragma unroll
@@ -586,21 +592,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
         sf1 = cvt8<T>(x, 1);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kDs1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- 2
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) qt[tt][db] = frag_t_swz(Qc, qb * 32, tt, db * 32);
+        for (int db = 0; db < ND; ++db) qt[tt][db] = frag_t_swz<T, D>(Qc, qb * 32, tt, db * 32);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) dk[db] = Mfma<T>::mma(qtp[0][db], sf0, dk[db]);
+      for (int db = 0; db < ND; ++db) dk[db] = Mfma<T>::mma(qtp[0][db], sf0, dk[db]);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) dk[db] = Mfma<T>::mma(qtp[1][db], sf1, dk[db]);
+      for (int db = 0; db < ND; ++db) dk[db] = Mfma<T>::mma(qtp[1][db], sf1, dk[db]);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         p[r] = fast_exp2(__builtin_fmaf(s[r], cs, -sel(l4, r)));
@@ -608,10 +614,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
       }
       pf0 = cvt8<T>(p, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- 3
@@ -619,10 +625,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
       const int nr = ((qb + 1) % NQB) * 32;
       if (qb + 1 < NQB) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(nq, nr, ks * 2);
+        for (int ks = 0; ks < NK; ++ks) qf[ks] = frag_r_swz<T, D>(nq, nr, ks * 2);
       }
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 0; ks < NK; ++ks) {
         asm("" : "+a"(of[ks]));  // dO rows are read into accumulator registers
         dp = Mfma<T>::mma(of[ks], vf[ks], dp);
       }
@@ -633,10 +639,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
       }
       pf1 = cvt8<T>(p, 1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (qb == NQB - 1) {
@@ -648,15 +654,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
         __syncthreads();
         if (t + 2 < ntiles) issue_tile(t + 2, t & 1);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qf[ks] = frag_r_swz(nq, nr, ks * 2);
+        for (int ks = 0; ks < NK; ++ks) qf[ks] = frag_r_swz<T, D>(nq, nr, ks * 2);
       }
       // ---- 4
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) of[ks] = frag_r_swz(nq + TR, nr, ks * 2);
+      for (int ks = 0; ks < NK; ++ks) of[ks] = frag_r_swz<T, D>(nq + TR, nr, ks * 2);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) dv[db] = Mfma<T>::mma(dt[0][db], pf0, dv[db]);
+      for (int db = 0; db < ND; ++db) dv[db] = Mfma<T>::mma(dt[0][db], pf0, dv[db]);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) dv[db] = Mfma<T>::mma(dt[1][db], pf1, dv[db]);
+      for (int db = 0; db < ND; ++db) dv[db] = Mfma<T>::mma(dt[1][db], pf1, dv[db]);
       {
         f32x16 x;
 #pragma unroll
@@ -664,10 +670,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
         sf0 = cvt8<T>(x, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       pc = p;
@@ -675,7 +681,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) qtp[tt][db] = qt[tt][db];
+        for (int db = 0; db < ND; ++db) qtp[tt][db] = qt[tt][db];
     }
   };
   int t = 0;
@@ -688,16 +694,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe_d128(BwdArgs a) {
     for (int r = 8; r < 16; ++r) x[r] = pc[r] * dpc[r];
     const V8<T> sf1 = cvt8<T>(x, 1);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) dk[db] = Mfma<T>::mma(qtp[0][db], sf0, dk[db]);
+    for (int db = 0; db < ND; ++db) dk[db] = Mfma<T>::mma(qtp[0][db], sf0, dk[db]);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) dk[db] = Mfma<T>::mma(qtp[1][db], sf1, dk[db]);
+    for (int db = 0; db < ND; ++db) dk[db] = Mfma<T>::mma(qtp[1][db], sf1, dk[db]);
   }
 
   if (kj < a.Sk) {
     T* dkrow = (T*)a.dk.p + b * a.dk.sb + h * a.dk.sh + (int64_t)kj * a.dk.ss;
     T* dvrow = (T*)a.dv.p + b * a.dv.sb + h * a.dv.sh + (int64_t)kj * a.dv.ss;
-    store_row4x4(dkrow, dk, a.scale, g);
-    store_row4x4(dvrow, dv, 1.f, g);
+    store_row4x4<T, ND>(dkrow, dk, a.scale, g);
+    store_row4x4<T, ND>(dvrow, dv, 1.f, g);
   }
 }
 
@@ -733,11 +739,12 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
 // Needs the 31-bit offsets the dK/dV kernel needs, for K and V.
 // NW waves of 32 query rows: 8, or 4 so that two workgroups share a CU and
 // one's prologue and epilogue overlap the other's tiles (either way two waves
-// per SIMD).
-template <class T, bool CAUSAL, int NW = 8>
-__global__ __launch_bounds__(NW * 64, 2) void dq_pipe_d128(BwdArgs a) {
+// per SIMD).  Head dim D = 128 or 64 (at 64: 12 MFMAs a block, same order).
+template <class T, bool CAUSAL, int NW = 8, int D = 128>
+__global__ __launch_bounds__(NW * 64, 2) void dq_pipe(BwdArgs a) {
   constexpr int BM = 32 * NW, BN = 64, NT = NW * 64, NKB = BN / 32;
-  constexpr int TR = BN * kD, BUF = 2 * TR;  // K rows, V rows
+  constexpr int TR = BN * D, BUF = 2 * TR;  // K rows, V rows
+  constexpr int NK = D / 16, ND = D / 32;   // k-steps of S and dP; column blocks of dQ
   __shared__ __attribute__((aligned(1024))) T smem[2 * BUF];
   (void)NT;
 
@@ -761,11 +768,11 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_pipe_d128(BwdArgs a) {
   const int ntiles = (kend + BN - 1) / BN;
   const unsigned lds0 = lds_addr(smem);
   const int ksb = (int)(a.k.ss * (int64_t)sizeof(T)), vsb = (int)(a.v.ss * (int64_t)sizeof(T));
-  const int klo = dma_lane_off<NW>(ksb), vlo = dma_lane_off<NW>(vsb);
+  const int klo = dma_lane_off<NW, D>(ksb), vlo = dma_lane_off<NW, D>(vsb);
   auto issue_tile = [&](int t) {
     const unsigned base = lds0 + (unsigned)((t & 1) * BUF * (int)sizeof(T));
-    tile_dma<BN, NW>(rk, base, klo, ksb, t * BN);
-    tile_dma<BN, NW>(rv, base + (unsigned)(TR * (int)sizeof(T)), vlo, vsb, t * BN);
+    tile_dma<BN, NW, D>(rk, base, klo, ksb, t * BN);
+    tile_dma<BN, NW, D>(rv, base + (unsigned)(TR * (int)sizeof(T)), vlo, vsb, t * BN);
   };
   // The first tile's buffer loads go out before the row loads, so that the
   // prologue waits for one memory round trip, not two.  (The row loads
@@ -773,14 +780,14 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_pipe_d128(BwdArgs a) {
   // the rows, which do not count these loads, are conservative.)
   if (ntiles > 0) issue_tile(0);
 
-  V8<T> qf[8], df[8];
+  V8<T> qf[NK], df[NK];
   const int qc = min(qi, a.Sq - 1);
   {
     const T* qrow = (const T*)a.q.p + b * a.q.sb + h * a.q.sh + (int64_t)qc * a.q.ss;
     const T* drow =
         (const T*)a.dout.p + b * a.dout.sb + h * a.dout.sh + (int64_t)qc * a.dout.ss;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < NK; ++ks) {
       qf[ks] = *reinterpret_cast<const V8<T>*>(qrow + ks * 16 + g * 8);
       df[ks] = *reinterpret_cast<const V8<T>*>(drow + ks * 16 + g * 8);
     }
@@ -797,7 +804,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_pipe_d128(BwdArgs a) {
     const T* orow = (const T*)a.o.p + b * a.o.sb + h * a.o.sh + (int64_t)qc * a.o.ss;
     float acc = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < NK; ++ks) {
       const V8<T> of = *reinterpret_cast<const V8<T>*>(orow + ks * 16 + g * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)df[ks][e], (float)of[e], acc);
@@ -808,9 +815,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_pipe_d128(BwdArgs a) {
   } else {
     dlt = valid ? a.delta[(int64_t)bh * a.Sq + qi] : 0.f;
   }
-  f32x16 dq[4];
+  f32x16 dq[ND];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dq[i] = zero16();
+  for (int i = 0; i < ND; ++i) dq[i] = zero16();
   const float cs = a.scale_log2;
 
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): rows and this wave's first-tile loads are in
@@ -831,26 +838,31 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_pipe_d128(BwdArgs a) {
       const int ks0 = k0 + kb * 32;
       if (CAUSAL && ks0 > qw + a.coff + 31) continue;
       // Products in a fixed order, each LDS fragment read issued four MFMAs
-      // ahead of its use: K rows for S, then V rows for dP, then the first
-      // half of transposed K for dQ; only VALU, SALU and global loads may be
-      // scheduled across the pinned order.
-      constexpr int kPin = 0x2 | 0x4 | 0x20;
-      V8<T> kf[8], vf[8], kt[2][4];
+      // ahead of its use: the reads go in the order of their uses (K rows
+      // for S, V rows for dP, then the two halves of transposed K for dQ),
+      // read j issued with product j - 4; only VALU, SALU and global loads
+      // may be scheduled across the pinned order.
+      constexpr int kPin = 0x2 | 0x4 | 0x20, kAhead = 4, kReads = 2 * NK + 2 * ND;
+      V8<T> kf[NK], vf[NK], kt[2][ND];
+      auto fetch = [&](int j) __attribute__((always_inline)) {
+        if (j < NK) kf[j] = frag_r_swz<T, D>(Kr, kb * 32, j * 2);
+        else if (j < 2 * NK) vf[j - NK] = frag_r_swz<T, D>(Vr, kb * 32, (j - NK) * 2);
+        else if (j < 2 * NK + ND) kt[0][j - 2 * NK] = frag_t_swz<T, D>(Kr, kb * 32, 0, (j - 2 * NK) * 32);
+        else if (j < kReads) kt[1][j - 2 * NK - ND] = frag_t_swz<T, D>(Kr, kb * 32, 1, (j - 2 * NK - ND) * 32);
+      };
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[ks] = frag_r_swz(Kr, kb * 32, ks * 2);
+      for (int j = 0; j < kAhead; ++j) fetch(j);
       __builtin_amdgcn_sched_barrier(kPin);
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        if (ks + 4 < 8) kf[ks + 4] = frag_r_swz(Kr, kb * 32, (ks + 4) * 2);
-        else vf[ks - 4] = frag_r_swz(Vr, kb * 32, (ks - 4) * 2);
+      for (int ks = 0; ks < NK; ++ks) {
+        fetch(ks + kAhead);
         s = Mfma<T>::mma(kf[ks], qf[ks], s);
         __builtin_amdgcn_sched_barrier(kPin);
       }
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        if (ks + 4 < 8) vf[ks + 4] = frag_r_swz(Vr, kb * 32, (ks + 4) * 2);
-        else kt[0][ks - 4] = frag_t_swz(Kr, kb * 32, 0, (ks - 4) * 32);
+      for (int ks = 0; ks < NK; ++ks) {
+        fetch(NK + ks + kAhead);
         dp = Mfma<T>::mma(vf[ks], df[ks], dp);
         __builtin_amdgcn_sched_barrier(kPin);
       }
@@ -868,13 +880,14 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_pipe_d128(BwdArgs a) {
       for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - dlt);
       const V8<T> sf0 = cvt8<T>(s, 0), sf1 = cvt8<T>(s, 1);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        kt[1][db] = frag_t_swz(Kr, kb * 32, 1, db * 32);
+      for (int db = 0; db < ND; ++db) {
+        fetch(2 * NK + db + kAhead);
         dq[db] = Mfma<T>::mma(kt[0][db], sf0, dq[db]);
         __builtin_amdgcn_sched_barrier(kPin);
       }
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < ND; ++db) {
+        fetch(2 * NK + ND + db + kAhead);
         dq[db] = Mfma<T>::mma(kt[1][db], sf1, dq[db]);
         __builtin_amdgcn_sched_barrier(kPin);
       }
@@ -889,39 +902,41 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_pipe_d128(BwdArgs a) {
 
   if (valid) {
     T* row = (T*)a.dq.p + b * a.dq.sb + h * a.dq.sh + (int64_t)qi * a.dq.ss;
-    store_row4x4(row, dq, a.scale, g);
+    store_row4x4<T, ND>(row, dq, a.scale, g);
   }
 }
 
-// Byte offsets of every Q and dO row the pipelined dK/dV kernel may address
-// (up to 3 tiles past Sq) fit in 31 bits, and rows do not overlap.
-bool dq_pipe_fits(const BwdArgs& a, int esize) {
+// Byte offsets of every K and V row the buffer-load dQ kernel may address
+// (up to 3 tiles past Sk) fit in 31 bits, and rows do not overlap.
+bool dq_pipe_fits(const BwdArgs& a, int esize, int D = kD) {
   const int64_t lim = (int64_t)1 << 31;
-  return a.k.ss >= kD && a.v.ss >= kD && ((int64_t)a.Sk + 3 * 64) * a.k.ss * esize < lim &&
+  return a.k.ss >= D && a.v.ss >= D && ((int64_t)a.Sk + 3 * 64) * a.k.ss * esize < lim &&
          ((int64_t)a.Sk + 3 * 64) * a.v.ss * esize < lim;
 }
 
-template <class T, bool CAUSAL, int NW = 8>
+template <class T, bool CAUSAL, int NW = 8, int D = 128>
 hipError_t launch_dq_pipe(const BwdArgs& a, hipStream_t s) {
   const int64_t grid = (((int64_t)a.Sq + 32 * NW - 1) / (32 * NW)) * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_pipe_d128<T, CAUSAL, NW>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dq_pipe<T, CAUSAL, NW, D>),
                          dim3((unsigned)grid), dim3(NW * 64), args, 0, s);
 }
 
-bool dkdv_pipe_fits(const BwdArgs& a, int esize) {
+// Byte offsets of every Q and dO row the pipelined dK/dV kernel may address
+// (up to 3 tiles past Sq) fit in 31 bits, and rows do not overlap.
+bool dkdv_pipe_fits(const BwdArgs& a, int esize, int D = kD) {
   const int64_t lim = (int64_t)1 << 31;
-  return a.q.ss >= kD && a.dout.ss >= kD && ((int64_t)a.Sq + 3 * 128) * a.q.ss * esize < lim &&
+  return a.q.ss >= D && a.dout.ss >= D && ((int64_t)a.Sq + 3 * 128) * a.q.ss * esize < lim &&
          ((int64_t)a.Sq + 3 * 128) * a.dout.ss * esize < lim;
 }
 
-template <class T, bool CAUSAL>
+template <class T, bool CAUSAL, int D = 128>
 hipError_t launch_dkdv_pipe(const BwdArgs& a, hipStream_t s) {
   const int64_t grid = (((int64_t)a.Sk + 127) / 128) * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_pipe_d128<T, CAUSAL>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_pipe<T, CAUSAL, D>),
                          dim3((unsigned)grid), dim3(256), args, 0, s);
 }
 
@@ -934,8 +949,14 @@ hipError_t launch_dkdv_pipe(const BwdArgs& a, hipStream_t s) {
 // tiles the staging registers push the non-causal kernel into spills.)
 // 6 = variant 5 with 4 waves, 128 query rows per workgroup and two workgroups
 // per CU (variant 1 runs instead where the offsets do not reach).
-int dq_fast_variants() { return 7; }
-TileCfg dq_fast_cfg(int v) {
+// Head dim 64: dq_pipe with 8 (variant 0) or 4 (variant 1) waves; where its
+// offsets do not reach, the caller runs a generic entry.
+int dq_fast_variants(int D) { return D == 128 ? 7 : D == 64 ? 2 : 0; }
+TileCfg dq_fast_cfg(int v, int D) {
+  if (D == 64) {
+    const int nw = v == 1 ? 4 : 8;
+    return TileCfg{32 * nw, 64, nw, 2 * 2 * 64 * 64 * 2};
+  }
   const int bn = v == 2 || v == 3 ? 32 : 64, nw = v == 1 || v == 6 ? 4 : 8;
   const int row_halfs = v >= 3 ? 2 * kD : 2 * kLSR + kLST;
   return TileCfg{32 * nw, bn, nw, 2 * bn * row_halfs * 2};
@@ -957,12 +978,30 @@ hipError_t launch_dq_variant(const BwdArgs& a, int v, int causal, hipStream_t s)
   }
   return hipErrorInvalidValue;
 }
-// Variants 5 and 6 run dq_pipe_d128 where its 31-bit offsets reach every row:
-// that kernel can form delta itself.
-bool dq_fast_fuses_delta(const BwdArgs& a, int v, int dtype) {
-  return (v == 5 || v == 6) && dq_pipe_fits(a, dtype == 1 ? 4 : 2);
+template <class T>
+hipError_t launch_dq_variant64(const BwdArgs& a, int v, int causal, hipStream_t s) {
+  switch (v) {
+    case 0: return causal ? launch_dq_pipe<T, true, 8, 64>(a, s) : launch_dq_pipe<T, false, 8, 64>(a, s);
+    case 1: return causal ? launch_dq_pipe<T, true, 4, 64>(a, s) : launch_dq_pipe<T, false, 4, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
-hipError_t launch_dq_fast(const BwdArgs& a, int v, int dtype, int causal, hipStream_t s) {
+// dQ variants 5 and 6 (D = 128) and every D = 64 variant run dq_pipe where
+// its 31-bit offsets reach every row: that kernel can form delta itself.
+bool dq_fast_fuses_delta(const BwdArgs& a, int v, int dtype, int D) {
+  const int es = dtype == 1 ? 4 : 2;
+  if (D == 64) return dq_pipe_fits(a, es, 64);
+  return (v == 5 || v == 6) && dq_pipe_fits(a, es);
+}
+bool dq_fast_runs(const BwdArgs& a, int dtype, int D) {
+  (void)dtype;
+  return D == 128 || dq_pipe_fits(a, 2, D);
+}
+hipError_t launch_dq_fast(const BwdArgs& a, int v, int dtype, int D, int causal, hipStream_t s) {
+  if (D == 64) {
+    if (dtype == 2) return launch_dq_variant64<bf16_t>(a, v, causal, s);
+    return launch_dq_variant64<half_t>(a, v, causal, s);
+  }
   if (dtype == 2) return launch_dq_variant<bf16_t>(a, v, causal, s);
   return launch_dq_variant<half_t>(a, v, causal, s);
 }
@@ -976,8 +1015,12 @@ hipError_t launch_dq_fast(const BwdArgs& a, int v, int dtype, int causal, hipStr
 // split between a score wave (K, dV) and an accumulate wave (V, dK) that
 // trade P through LDS, 64-query tiles in three buffers (fa_bwd_split.hip;
 // variant 4 runs instead where its 31-bit offsets do not reach every row).
-int dkdv_fast_variants() { return 6; }
-TileCfg dkdv_fast_cfg(int v) {
+// Head dim 64: the software-pipelined kernel (variant 0; with two waves per
+// SIMD, 256 registers a wave, it spills); where its offsets do not reach, the
+// caller runs a generic entry.
+int dkdv_fast_variants(int D) { return D == 128 ? 6 : D == 64 ? 1 : 0; }
+TileCfg dkdv_fast_cfg(int v, int D) {
+  if (D == 64) return TileCfg{128, 128, 4, 2 * 2 * 128 * 64 * 2 + 2 * 2 * 128 * 4};
   if (v == 5) return TileCfg{64, 128, 8, dkdv_split_lds()};
   const int bm = v == 1 ? 32 : v >= 3 ? 128 : 64, nw = 4;
   const int row_halfs = v >= 2 ? 2 * kD : 2 * kLSR + 2 * kLST;
@@ -999,7 +1042,22 @@ hipError_t launch_dkdv_variant(const BwdArgs& a, int v, int causal, hipStream_t 
   }
   return hipErrorInvalidValue;
 }
-hipError_t launch_dkdv_fast(const BwdArgs& a, int v, int dtype, int causal, hipStream_t s) {
+template <class T>
+hipError_t launch_dkdv_variant64(const BwdArgs& a, int v, int causal, hipStream_t s) {
+  switch (v) {
+    case 0: return causal ? launch_dkdv_pipe<T, true, 64>(a, s) : launch_dkdv_pipe<T, false, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+bool dkdv_fast_runs(const BwdArgs& a, int dtype, int D) {
+  (void)dtype;
+  return D == 128 || dkdv_pipe_fits(a, 2, D);
+}
+hipError_t launch_dkdv_fast(const BwdArgs& a, int v, int dtype, int D, int causal, hipStream_t s) {
+  if (D == 64) {
+    if (dtype == 2) return launch_dkdv_variant64<bf16_t>(a, v, causal, s);
+    return launch_dkdv_variant64<half_t>(a, v, causal, s);
+  }
   if (dtype == 2) return launch_dkdv_variant<bf16_t>(a, v, causal, s);
   return launch_dkdv_variant<half_t>(a, v, causal, s);
 }
