@@ -46,13 +46,10 @@ def hipcc() -> str:
 
 
 # Any kernel that uses scratch (spilled or stack-allocated) memory is a build
-# error: spilling tile configurations are pruned from the tile tables.  The
-# one exception is the generic fp32 head-dim-128 non-causal dK/dV kernel
-# (92 bytes per lane with VGPR-form MFMAs and K, V in accumulator registers;
-# the only candidate whose LDS fits), kept so that the shape has a kernel; a
-# four-pass version that does not spill ran 63 % slower.  (Mangled-name
-# fragment of the allowed instantiation.)
-ALLOWED_SCRATCH = ("11dkdv_kernelIfLi128ELi32ELi4ELi1ELb0E",)
+# error: spilling tile configurations are pruned from the tile tables, and no
+# kernel is exempt.  (Mangled-name fragments of allowed instantiations would
+# go here.)
+ALLOWED_SCRATCH: tuple = ()
 
 
 def _scratch_kernels(remarks: str):

@@ -100,9 +100,8 @@ constexpr Tile tile_at(int dt, int i) { return dt == 0 ? kTilesH[i] : kTilesF[i]
 constexpr int num_tiles_raw(int dt) { return dt == 0 ? kNumH : kNumF; }
 // A tile survives if its LDS fits and its kernel compiles without spilling
 // (measured with hipcc for gfx950: at head dim 128 the 16-bit 8-wave kernel
-// spills, and every fp32 candidate does; of those only the 4-wave one, which
-// spills least, is kept, so that fp32 D = 128 has a kernel.  The build fails
-// on any other kernel that uses scratch memory).
+// spills, and so does the fp32 2-wave one; the build fails on any kernel that
+// uses scratch memory).
 constexpr bool tile_ok(int dt, int D, int i) {
   return lds_bytes(dt == 0 ? 2 : 4, D, tile_at(dt, i).bm, tile_at(dt, i).nb) <= kLdsMax &&
          !(D == 128 && dt == 0 && tile_at(dt, i).nw == 8) &&

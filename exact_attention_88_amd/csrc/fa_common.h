@@ -241,9 +241,12 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_rows(const T* lds, int rb
 
 // 32x32 block C = X[rbase.., :] * B over the head dim, X read row-wise from
 // LDS (frag_rows) and B from registers (bf[ks], ks < D/KSTEP).  For fp32 the
-// contraction is split into chains of 16 head-dim elements that are summed
-// pairwise, which keeps the rounding of long dot products of large scores
-// (peaked softmax) well inside fp32 tolerances; fp16 uses one chain.
+// contraction is split into chains of 16 head-dim elements whose sums are
+// combined by compensated (Kahan) summation, which keeps the rounding of long
+// dot products of large scores (peaked softmax) well inside fp32 tolerances
+// with only two partial sums live; every fp32 kernel forms its scores this
+// way, so the backward's recomputed scores match the forward's bit for bit
+// and their rounding cancels in P = exp(S - LSE).  fp16 uses one chain.
 template <class T, int D, int LS>
 __device__ __forceinline__ f32x16 dot_block(const T* lds, int rbase,
                                             const typename Mfma<T>::frag* bf) {
@@ -258,24 +261,28 @@ __device__ __forceinline__ f32x16 dot_block(const T* lds, int rbase,
   } else {
     constexpr int CHAIN = 8;  // MFMA steps (16 elements) per partial sum
     constexpr int NCH = NKS / CHAIN;  // 1, 2, 4 or 8
-    constexpr int NLV = NCH == 8 ? 4 : NCH == 4 ? 3 : NCH == 2 ? 2 : 1;
-    // Pairwise summation with a carry stack: level l holds the sum of 2^l
-    // chains, so at most log2(NCH) partial sums are live at once.
-    f32x16 lvl[NLV];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    auto chain = [&](int c) {
       f32x16 x = zero16();
 #pragma unroll
       for (int k = 0; k < CHAIN; ++k) {
         const int ks = c * CHAIN + k;
         x = M::mma(frag_rows<T, LS>(lds, rbase, ks * M::KSTEP), bf[ks], x);
       }
-      int l = 0;
+      return x;
+    };
+    f32x16 acc = chain(0), err = zero16();
 #pragma unroll
-      for (; l < NLV - 1 && ((c >> l) & 1); ++l) x = lvl[l] + x;
-      lvl[l] = x;
+    for (int c = 1; c < NCH; ++c) {
+      const f32x16 x = chain(c);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float y = x[r] - err[r];
+        const float t = acc[r] + y;
+        err[r] = (t - acc[r]) - y;
+        acc[r] = t;
+      }
     }
-    return lvl[NLV - 1];
+    return acc;
   }
 }
 
