@@ -68,11 +68,17 @@ template <> struct Mfma<float> {
 // Workgroup -> (block rank within its (b,h), b*h).  Workgroups go out to the
 // 8 XCDs round robin (id % 8); each (b,h)'s nb blocks stay on one XCD so that
 // its L2 serves their shared K/V (or Q/dO) stream.  With by_rank, and whole
-// heads on every XCD, an XCD's workgroups go out rank by rank across its
-// heads (rank 0 of every head first) rather than head by head: the causal
-// kernels give rank 0 the most work, so this is longest-first scheduling and
-// the launch does not end on the long blocks of the XCD's last head.  The
-// causal forward, dQ and dK/dV kernels take it.
+// heads on every XCD, an XCD's heads go out in groups of kHeadGroup, and a
+// group's workgroups rank by rank across its heads (rank 0 of every head of
+// the group first) rather than head by head: the causal kernels give rank 0
+// the most work, so this is longest-first scheduling within the group and the
+// launch does not end on the long blocks of the XCD's last head, while at
+// most a group's heads' streams share the XCD's L2 at a time (rank by rank
+// across all of an XCD's heads, at S = 512 and 1024 with 32 and more heads
+// an XCD, the dQ and dK/dV kernels ran 5-10 % slower: the heads' streams no
+// longer fit its L2).  The causal forward, dQ and dK/dV kernels take it.
+constexpr int kHeadGroup = 4;
+
 __device__ __forceinline__ void xcd_block(int nb, bool by_rank, int& rank, int& bh) {
   const int n = gridDim.x, id = blockIdx.x;
   int L = id;
@@ -80,8 +86,10 @@ __device__ __forceinline__ void xcd_block(int nb, bool by_rank, int& rank, int& 
     const int per = n / 8, x = id % 8, slot = id / 8;
     if (by_rank && per % nb == 0) {
       const int hx = per / nb;
-      rank = slot / hx;
-      bh = x * hx + slot % hx;
+      const int gh = hx % kHeadGroup == 0 ? kHeadGroup : hx;
+      const int grp = slot / (gh * nb), s2 = slot - grp * gh * nb;
+      rank = s2 / gh;
+      bh = x * hx + grp * gh + s2 % gh;
       return;
     }
     L = x * per + slot;
