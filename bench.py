@@ -374,10 +374,11 @@ def length_sweep(fa, torch, steps, warmup, flush, keep_samples):
     return out, samples
 
 
-def probe_rates(fa, torch):
+def probe_rates(torch):
     """Measured ceilings on this device: dense fp16 MFMA TFLOP/s and v_exp_f32
-    exponentials per second (the library's probes, timed with HIP events on
-    the stream they run on after a warm-up launch)."""
+    exponentials per second (the probes of libfa_probe.so, timed with HIP
+    events on the stream they run on after a warm-up launch)."""
+    from exact_attention_88_amd import probe as fa
     n = fa.fa_probe_threads()
     sink = torch.empty(n, device="cuda")
     out = {}
@@ -699,7 +700,7 @@ def main():
     # Secondary ceilings: the measured MFMA rate, and the exponential rate
     # against the step's exponentials (one per visible score in the forward,
     # the dQ and the dK/dV kernels: 3 x B*H*Sq*Sk, halved when causal).
-    probes = probe_rates(fa, torch)
+    probes = probe_rates(torch)
     n_exp = 3 * case.B * case.H * case.Sq * case.Sk / (2 if case.causal else 1)
     probes["exp2_floor_ms_per_step"] = round(n_exp / probes["exp2_per_s"] * 1e3, 4)
     line["probes"] = probes

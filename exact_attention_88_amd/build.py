@@ -1,7 +1,9 @@
-"""Build the HIP library ``libfa.so`` in-tree for gfx950.
+"""Build the HIP libraries in-tree for gfx950.
 
-Each ``csrc/*.hip`` translation unit is compiled to an object in parallel and
-then linked into ``exact_attention_88_amd/libfa.so``.  Run as
+Each ``csrc/*.hip`` translation unit is compiled to an object in parallel;
+the attention sources are linked into ``exact_attention_88_amd/libfa.so``
+(``include/fa.h``) and the measurement probes into
+``exact_attention_88_amd/libfa_probe.so`` (``include/fa_probe.h``).  Run as
 ``python -m exact_attention_88_amd.build``.
 """
 from __future__ import annotations
@@ -17,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+PROBE_LIB = os.path.join(PKG, "libfa_probe.so")
 
 ARCH = "gfx950"
 FLAGS = [
@@ -35,7 +38,8 @@ FLAGS = [
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 EXTRA_FLAGS = {"fa_bwd_f16.hip": _VGPR_FORM, "fa_bwd_dkdv.hip": _VGPR_FORM, "fa_bwd_dq.hip": _VGPR_FORM}
 SOURCES = ["fa_fwd.hip", "fa_fwd_f16.hip", "fa_bwd_dkdv.hip", "fa_bwd_dq.hip", "fa_bwd_f16.hip",
-           "fa_bwd_split.hip", "fa_probe.hip", "fa_api.hip"]
+           "fa_bwd_split.hip", "fa_api.hip"]
+PROBE_SOURCES = ["fa_probe.hip"]
 
 
 def hipcc() -> str:
@@ -79,19 +83,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {os.path.basename(PROBE_LIB)}")
     return LIB
 
 

@@ -390,12 +390,4 @@ const char* fa_version(void) {
       HIP_VERSION_PATCH) "; " __VERSION__;
 }
 
-int64_t fa_probe_threads(void) { return (int64_t)fa::probe_workgroups() * 256; }
-
-int fa_probe(int kind, int iters, float* sink, void* stream) {
-  if (kind < 0 || kind > 1 || iters < 1) return FA_ERR_SHAPE;
-  if (!sink) return FA_ERR_NULL;
-  return hip_status(fa::launch_probe(kind, iters, sink, (hipStream_t)stream));
-}
-
 }  // extern "C"

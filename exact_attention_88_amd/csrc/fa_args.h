@@ -82,10 +82,6 @@ bool dq_can_fuse_delta(const BwdArgs& a, int dtype, int D, int tile);
 
 hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int D, hipStream_t s);
 
-// Measurement probes (fa_probe.hip): kind 0 = fp16 MFMA, 1 = v_exp_f32.
-int probe_workgroups();
-hipError_t launch_probe(int kind, int iters, float* sink, hipStream_t s);
-
 // Tuned 16-bit (fp16, bf16) backward kernels for head dims 128 and 64
 // (fa_bwd_f16.hip); *_fast_runs tells whether the launcher can take these
 // arguments (else a generic entry runs).

@@ -1,5 +1,6 @@
-// Measurement probes: the rates the attention kernels are bounded by, taken
-// on the device they run on.
+// Measurement probes (libfa_probe.so, declared in include/fa_probe.h): the
+// rates the attention kernels of libfa.so are bounded by, taken on the device
+// they run on.
 //   * the dense fp16 MFMA rate: waves issuing back-to-back independent
 //     v_mfma_f32_32x32x16_f16 on register operands (the ceiling of every
 //     matrix product in the forward and backward);
@@ -12,7 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "fa_args.h"
+#include "../../include/fa_probe.h"
 #include "fa_common.h"
 
 namespace fa {
@@ -80,3 +81,15 @@ hipError_t launch_probe(int kind, int iters, float* sink, hipStream_t s) {
 }
 
 }  // namespace fa
+
+extern "C" {
+
+int64_t fa_probe_threads(void) { return (int64_t)fa::probe_workgroups() * 256; }
+
+int fa_probe(int kind, int iters, float* sink, void* stream) {
+  if (kind < 0 || kind > 1 || iters < 1) return FA_ERR_SHAPE;
+  if (!sink) return FA_ERR_NULL;
+  return fa::launch_probe(kind, iters, sink, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

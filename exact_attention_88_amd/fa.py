@@ -14,7 +14,7 @@ import ctypes
 import os
 
 __all__ = ["FAError", "fa_fwd", "fa_bwd", "fa_fwd_tile", "fa_bwd_tile", "fa_bwd_stage",
-           "fa_bwd_noalloc", "fa_probe",
+           "fa_bwd_noalloc",
            "fa_tile_count",
            "fa_tile_info", "fa_tile_default", "fa_status_string", "fa_last_hip_error", "fa_version",
            "lib_path",
@@ -26,8 +26,7 @@ FA_PASS_FWD, FA_PASS_BWD_DKDV, FA_PASS_BWD_DQ = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_fwd_tile", "fa_bwd_tile", "fa_bwd_stage",
                     "fa_bwd_noalloc", "fa_tile_count", "fa_tile_info", "fa_tile_default",
-                    "fa_status_string", "fa_last_hip_error", "fa_version", "fa_probe",
-                    "fa_probe_threads")
+                    "fa_status_string", "fa_last_hip_error", "fa_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -91,10 +90,6 @@ def _load():
     lib.fa_last_hip_error.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = ctypes.c_char_p
-    lib.fa_probe.argtypes = [c_int, c_int, vp, vp]
-    lib.fa_probe.restype = c_int
-    lib.fa_probe_threads.argtypes = []
-    lib.fa_probe_threads.restype = i64
     return lib
 
 
@@ -343,21 +338,6 @@ def fa_bwd_stage(stage, tile_id, q, k, v, o, dout, lse, causal=False, scale=None
     t = (tile_id, tile_id)
     return fa_bwd_tile(t[0], t[1], q, k, v, o, dout, lse, causal, scale, dq, dk, dv, delta,
                        _stage=stage)
-
-
-def fa_probe_threads() -> int:
-    return int(_lib.fa_probe_threads())
-
-
-def fa_probe(kind, iters, sink):
-    """Launch a measurement probe (0 = fp16 MFMA, 1 = v_exp_f32) writing one
-    float per thread to ``sink`` (float32, at least fa_probe_threads()
-    elements, on the GPU) on torch's current stream; see ``fa_probe`` in
-    include/fa.h for the work per launch."""
-    import torch
-    if not sink.is_cuda or sink.dtype != torch.float32 or sink.numel() < fa_probe_threads():
-        raise ValueError("sink must be a float32 device tensor of fa_probe_threads() elements")
-    _check(_lib.fa_probe(int(kind), int(iters), _ptr(sink), _stream_ptr(sink)))
 
 
 def raw_lib():

@@ -1,5 +1,6 @@
 """CPU checks of the C boundary: the library loads, exports every function
-that include/fa.h declares, and rejects bad arguments before any HIP call.
+that include/fa.h declares, and rejects bad arguments before any HIP call;
+the same for the probe library and include/fa_probe.h.
 
 No call here reaches a kernel launch: every call either fails validation or
 is a documented no-op, so these run without a GPU.
@@ -12,6 +13,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "fa_probe.h")
 
 fa = pytest.importorskip("exact_attention_88_amd.fa")
 lib = fa.raw_lib()
@@ -21,10 +23,17 @@ FAKE = 0x10000  # a non-null address that is never dereferenced by a rejected ca
 S = I64x4(1 << 20, 1 << 16, 128, 1)
 
 
-def _declared():
-    txt = open(HEADER).read()
+def _declared(header=HEADER):
+    txt = open(header).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", txt)))
+
+
+def _exported(path):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                         text=True, check=True).stdout
+    return set(re.findall(r"\bT (fa_[a-z_0-9]+)", out))
 
 
 def test_header_declarations_match_binding():
@@ -32,13 +41,20 @@ def test_header_declarations_match_binding():
 
 
 def test_library_exports_every_declared_symbol():
-    import subprocess
-    out = subprocess.run(["nm", "-D", "--defined-only", fa.lib_path()], capture_output=True,
-                         text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (fa_[a-z_0-9]+)", out))
+    exported = _exported(fa.lib_path())
     for name in _declared():
         assert name in exported, name
         assert hasattr(lib, name)
+
+
+def test_probe_library_exports_its_header_and_nothing_of_the_attention_api():
+    from exact_attention_88_amd import probe
+    assert _declared(PROBE_HEADER) == sorted(probe.EXPORTED_SYMBOLS)
+    exported = _exported(probe.lib_path())
+    for name in _declared(PROBE_HEADER):
+        assert name in exported, name
+    assert not exported & set(_declared())            # no attention entry point
+    assert not _exported(fa.lib_path()) & set(_declared(PROBE_HEADER))  # and no probe in libfa
 
 
 def test_version_and_status_strings():
@@ -199,11 +215,13 @@ def test_tile_default_follows_the_swept_table(pass_id):
 
 
 def test_probe_rejects_bad_arguments_before_any_launch():
+    from exact_attention_88_amd import probe
+    plib = probe.raw_lib()
     sink = ctypes.c_void_p(FAKE)
-    assert lib.fa_probe(2, 10, sink, None) == -2     # unknown kind
-    assert lib.fa_probe(-1, 10, sink, None) == -2
-    assert lib.fa_probe(0, 0, sink, None) == -2      # no iterations
-    assert lib.fa_probe(1, 10, None, None) == -1     # no sink
+    assert plib.fa_probe(2, 10, sink, None) == -2     # unknown kind
+    assert plib.fa_probe(-1, 10, sink, None) == -2
+    assert plib.fa_probe(0, 0, sink, None) == -2      # no iterations
+    assert plib.fa_probe(1, 10, None, None) == -1     # no sink
 
 
 def _bwd_noalloc(B=1, H=1, Sq=8, Sk=8, D=64, dtype=0, causal=0, scale=0.125, ptrs=None):

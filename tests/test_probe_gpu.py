@@ -8,7 +8,7 @@ torch = pytest.importorskip("torch")
 
 @pytest.mark.parametrize("kind", [0, 1], ids=["mfma", "exp2"])
 def test_probe_runs_and_fills_the_sink(kind):
-    from exact_attention_88_amd import fa
+    from exact_attention_88_amd import probe as fa
     n = fa.fa_probe_threads()
     assert n > 0 and n % 256 == 0
     sink = torch.full((n,), float("nan"), device="cuda")
