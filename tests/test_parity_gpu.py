@@ -438,6 +438,18 @@ def test_long_context_bf16_sampled():
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("dname,causal", [("f16", True), ("f16", False), ("bf16", True)])
+def test_long_context_d64_sampled(dname, causal):
+    """Head dim 64 at the long workload's size (B=1, H=16, S=16384): the tuned
+    D=64 forward, dQ and dK/dV kernels over many tiles and every XCD, sampled
+    rows against the oracle."""
+    case = W.Case(f"long_d64_{dname}_{'c' if causal else 'nc'}", 1, 16, 16384, 16384, 64, dname,
+                  causal, seed=80 + (2 if dname == "bf16" else 0) + int(causal))
+    x, got = run_case(case)
+    check_sampled(case, x, got, _spread_heads(case, 2), seed=2)
+
+
+@pytest.mark.slow
 @pytest.mark.parametrize("case", W.sweep_cases(), ids=lambda c: c.name)
 def test_length_sweep_sampled(case):
     x, got = run_case(case)
