@@ -122,8 +122,8 @@ int fa_fwd(const void* q, const int64_t q_strides[4],
  * [B,H,Sk,D] are overwritten.  `scale` must be the forward's (finite, > 0,
  * else FA_ERR_SCALE).  The kernels run in order on `stream`: the
  * rowsum, the dQ kernel, the dK/dV kernel; where the dQ kernel can form delta
- * from the query rows it holds (16-bit, D = 128, 16-byte-aligned rows) there
- * is no separate rowsum launch and the dQ kernel writes delta_ws.
+ * from the query rows it holds (16-bit, D = 128 or 64, 16-byte-aligned rows)
+ * there is no separate rowsum launch and the dQ kernel writes delta_ws.
  */
 int fa_bwd(const void* q, const int64_t q_strides[4],
            const void* k, const int64_t k_strides[4],
@@ -224,7 +224,7 @@ int fa_bwd_tile(int dkdv_tile_id, int dq_tile_id,
  * 2 = the dQ kernel (writes dq), 1 = the dK/dV
  * kernel (reads delta_ws, writes dk, dv; q/o/dout/lse/dq may be NULL when
  * Sq == 0).  Where the chosen dQ kernel can form delta from the rows it
- * holds (16-bit, D = 128, 16-byte-aligned rows: the default there), stage 0
+ * holds (16-bit, D = 128 or 64, 16-byte-aligned rows: the default there), stage 0
  * launches nothing and stage 2 writes delta_ws itself; otherwise stage 2
  * reads it.  Running stages 0, 2, 1 in that order on one stream is exactly
  * fa_bwd_tile.  For per-kernel timing and profiling.
