@@ -392,6 +392,9 @@ int dkdv_tile_default(int dtype, int D, int64_t Sq, int64_t Sk, int causal) {
   // swizzled single-copy layout, buffer loads into LDS) measured fastest on
   // MI355X at every length from 512 to 16384, causal and not.
   if (table_dt(dtype) == 0 && D == 128) return 4;
+  // 16-bit, D = 64: the same kernel with two waves per SIMD, fastest at every
+  // length from 128 to 16384.
+  if (table_dt(dtype) == 0 && D == 64) return 1;
   return 0;
 }
 

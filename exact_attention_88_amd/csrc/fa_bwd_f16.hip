@@ -429,8 +429,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_f16_d128(BwdArgs a) {
 //     are never stored.
 // Needs 32-bit byte offsets: (Sq + 3*128) * row stride * 2 bytes < 2^31 for
 // Q and dO, and a row stride of at least 128 elements (checked on the host).
-template <class T, bool CAUSAL, int D = 128>
-__global__ __launch_bounds__(256, 1) void dkdv_pipe(BwdArgs a) {
+// WPE: waves per SIMD the registers must allow (1, or 2 at D = 64: two
+// workgroups per CU; the operands then stay in architectural registers).
+template <class T, bool CAUSAL, int D = 128, int WPE = 1>
+__global__ __launch_bounds__(256, WPE) void dkdv_pipe(BwdArgs a) {
   constexpr int BM = 128, NW = 4, BN = 32 * NW, NQB = BM / 32, TR = BM * D, BUF = 2 * TR;
   constexpr int NK = D / 16, ND = D / 32;  // k-steps of S and dP; column blocks of dK and dV
   // Per scheduling group (one MFMA each): LDS reads of phase 1, VALU.
@@ -522,10 +524,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe(BwdArgs a) {
     // S and dP products and the dK and dV sums (this file is built with the
     // VGPR accumulator form of the MFMAs, so S and dP reach the
     // softmax-gradient arithmetic without a v_accvgpr_read per element).
+    if constexpr (WPE == 1) {
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      asm("" : "+a"(kf[ks]));
-      asm("" : "+a"(vf[ks]));
+      for (int ks = 0; ks < NK; ++ks) {
+        asm("" : "+a"(kf[ks]));
+        asm("" : "+a"(vf[ks]));
+      }
     }
   }
   if (ntiles > 0) {
@@ -629,7 +633,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_pipe(BwdArgs a) {
       }
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        asm("" : "+a"(of[ks]));  // dO rows are read into accumulator registers
+        if constexpr (WPE == 1) asm("" : "+a"(of[ks]));  // dO rows are read into accumulator registers
         dp = Mfma<T>::mma(of[ks], vf[ks], dp);
       }
 #pragma unroll
@@ -931,12 +935,12 @@ bool dkdv_pipe_fits(const BwdArgs& a, int esize, int D = kD) {
          ((int64_t)a.Sq + 3 * 128) * a.dout.ss * esize < lim;
 }
 
-template <class T, bool CAUSAL, int D = 128>
+template <class T, bool CAUSAL, int D = 128, int WPE = 1>
 hipError_t launch_dkdv_pipe(const BwdArgs& a, hipStream_t s) {
   const int64_t grid = (((int64_t)a.Sk + 127) / 128) * a.B * a.H;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   void* args[] = {const_cast<void*>(static_cast<const void*>(&a))};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_pipe<T, CAUSAL, D>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&dkdv_pipe<T, CAUSAL, D, WPE>),
                          dim3((unsigned)grid), dim3(256), args, 0, s);
 }
 
@@ -1015,10 +1019,11 @@ hipError_t launch_dq_fast(const BwdArgs& a, int v, int dtype, int D, int causal,
 // split between a score wave (K, dV) and an accumulate wave (V, dK) that
 // trade P through LDS, 64-query tiles in three buffers (fa_bwd_split.hip;
 // variant 4 runs instead where its 31-bit offsets do not reach every row).
-// Head dim 64: the software-pipelined kernel (variant 0; with two waves per
-// SIMD, 256 registers a wave, it spills); where its offsets do not reach, the
+// Head dim 64: the software-pipelined kernel with one wave per SIMD (variant
+// 0) or two (variant 1: two workgroups per CU, K, V and dO rows in
+// architectural registers, 256 a wave); where its offsets do not reach, the
 // caller runs a generic entry.
-int dkdv_fast_variants(int D) { return D == 128 ? 6 : D == 64 ? 1 : 0; }
+int dkdv_fast_variants(int D) { return D == 128 ? 6 : D == 64 ? 2 : 0; }
 TileCfg dkdv_fast_cfg(int v, int D) {
   if (D == 64) return TileCfg{128, 128, 4, 2 * 2 * 128 * 64 * 2 + 2 * 2 * 128 * 4};
   if (v == 5) return TileCfg{64, 128, 8, dkdv_split_lds()};
@@ -1046,6 +1051,7 @@ template <class T>
 hipError_t launch_dkdv_variant64(const BwdArgs& a, int v, int causal, hipStream_t s) {
   switch (v) {
     case 0: return causal ? launch_dkdv_pipe<T, true, 64>(a, s) : launch_dkdv_pipe<T, false, 64>(a, s);
+    case 1: return causal ? launch_dkdv_pipe<T, true, 64, 2>(a, s) : launch_dkdv_pipe<T, false, 64, 2>(a, s);
   }
   return hipErrorInvalidValue;
 }
