@@ -457,24 +457,25 @@ def test_length_sweep_sampled(case):
 
 
 @pytest.mark.slow
-def test_wide_row_stride_takes_the_64bit_path():
+@pytest.mark.parametrize("D", [128, 64])
+def test_wide_row_stride_takes_the_64bit_path(D):
     """Rows 64 Ki elements apart (a [S, 512, 128] store seen one head at a
-    time): byte offsets of the last key rows pass 2^31, beyond the 32-bit
-    offsets of the buffer-load kernels, so the library must run the
-    register-staged kernels with 64-bit addressing; sampled rows against the
-    oracle."""
+    time, its first D columns): byte offsets of the last key rows pass 2^31,
+    beyond the 32-bit offsets of the buffer-load kernels, so the library must
+    run kernels with 64-bit addressing (register-staged at D = 128, the
+    generic ones at D = 64); sampled rows against the oracle."""
     fa = _fa()
     S, stride = 16640, 512 * 128
-    case = W.Case("wide_stride_f16_causal", 1, 1, S, S, 128, "f16", True, seed=71)
+    case = W.Case(f"wide_stride_f16_causal_D{D}", 1, 1, S, S, D, "f16", True, seed=71)
     assert (S + 3 * 64) * stride * 2 >= 1 << 31  # past every kernel's 31-bit limit
     x = W.make_inputs(case)
     dev = {}
     for n, a in x.items():
         store = torch.empty((S, 512, 128), dtype=torch.float16, device="cuda")
-        store[:, 3] = torch.from_numpy(np.ascontiguousarray(a[0, 0])).cuda()
-        dev[n] = store[:, 3].unsqueeze(0).unsqueeze(0)  # [1, 1, S, 128], row stride 65536
+        store[:, 3, :D] = torch.from_numpy(np.ascontiguousarray(a[0, 0])).cuda()
+        dev[n] = store[:, 3, :D].unsqueeze(0).unsqueeze(0)  # [1, 1, S, D], row stride 65536
         assert dev[n].stride(2) == stride
-    o = torch.full((1, 1, S, 128), float("nan"), dtype=torch.float16, device="cuda")
+    o = torch.full((1, 1, S, D), float("nan"), dtype=torch.float16, device="cuda")
     lse = U.nan_vec((1, 1, S))
     print(f"[gpu] fwd {case.name}", flush=True)
     fa.fa_fwd(dev["q"], dev["k"], dev["v"], True, case.scale, out=o, lse=lse)
