@@ -70,6 +70,8 @@ def parse():
                     help="optional path: also write the length sweep's records there, one JSON line each")
     ap.add_argument("--no-bf16", action="store_true",
                     help="skip the secondary bfloat16 timing of the same workload")
+    ap.add_argument("--no-d64", action="store_true",
+                    help="skip the secondary head-dim-64 timing of the same workload")
     ap.add_argument("--no-flush", action="store_true",
                     help="time back-to-back steps without the cache flush (for comparison only)")
     ap.add_argument("--seq", type=int, default=0,
@@ -696,6 +698,23 @@ def main():
                         "ms_per_step": round(br["median"]["step"], 4), "steps": bsteps,
                         "kernel_ms": {n: round(v, 4) for n, v in br["median"].items() if n != "step"}}
         del bdev, br
+    if not args.no_d64:
+        # Secondary figure: the same workload at head dim 64 (the mid
+        # workload's head dim; fresh draws of that shape), same protocol, its
+        # own flop count.
+        import dataclasses
+        dcase = dataclasses.replace(case, name="long_d64_causal", D=64)
+        _, ddev = make_device_inputs(dcase, torch)
+        dff = fwd_flops(dcase.B, dcase.H, dcase.Sq, dcase.Sk, dcase.D, dcase.causal)
+        dsteps = max(5, args.steps // 2)
+        dr = time_path(fa, torch, dcase, ddev, dsteps, args.warmup, flush, min_warm_s=0.3)
+        line["d64"] = {"workload": f"B={dcase.B} H={dcase.H} S={dcase.Sq} D=64 causal fp16",
+                       "fwd_tflops": round(dff / (dr["median"]["fwd"] * 1e-3) / 1e12, 2),
+                       "fwdbwd_tflops": round(3.5 * dff / (dr["median"]["step"] * 1e-3) / 1e12, 2),
+                       "ms_per_step": round(dr["median"]["step"], 4), "steps": dsteps,
+                       "kernel_ms": {n: round(v, 4) for n, v in dr["median"].items() if n != "step"},
+                       "tiles": tiles_used(fa, dcase)}
+        del ddev, dr
     line["memory"] = peak_memory(torch, case, dev)
     # Secondary ceilings: the measured MFMA rate, and the exponential rate
     # against the step's exponentials (one per visible score in the forward,
