@@ -1,5 +1,6 @@
 // Backward dK/dV and dQ kernels for 16-bit inputs (fp16, bf16) with head dim
-// 128 on gfx950: the tuned path.
+// 128 (and, for the pipelined dK/dV and buffer-load dQ kernels, 64) on
+// gfx950: the tuned path.
 //
 // Same method as the generic backward kernels ("Triton FlashAttention",
 // opening summary: key-side and query-side gradients from two kernels, no

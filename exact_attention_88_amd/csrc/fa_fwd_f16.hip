@@ -1,5 +1,5 @@
-// Forward attention for 16-bit inputs (fp16, bf16) with head dim 128 on
-// gfx950: the tuned path.
+// Forward attention for 16-bit inputs (fp16, bf16) with head dim 128 (and,
+// for the buffer-load kernel, 64) on gfx950: the tuned path.
 //
 // Same method as the generic forward kernel ("FlashAttention-2 from PyTorch to
 // Triton": online softmax over streamed K/V tiles, one program per query tile;
