@@ -41,7 +41,9 @@ def _both(case):
      W.Case("na_small_f16_c", 1, 2, 333, 333, 128, "f16", True, seed=902)),
     (W.Case("na_big_f32_nc", 2, 4, 700, 900, 64, "f32", False, seed=903),
      W.Case("na_small_bf16_br", 1, 3, 200, 450, 32, "bf16", 2, seed=904, layout="bshd")),
-], ids=["f16-d128", "generic"])
+    (W.Case("na_big_f16_d64_c", 2, 8, 2048, 2048, 64, "f16", True, seed=905),
+     W.Case("na_small_bf16_d64_nc", 1, 2, 333, 333, 64, "bf16", False, seed=906)),
+], ids=["f16-d128", "generic", "d64"])
 def test_noalloc_backward_matches_fa_bwd_twice(first, second):
     _both(first)
     _both(second)
