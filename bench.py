@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--seq", type=int, default=0,
                     help="time the length-sweep workload at this S (fp16 causal, H=16, D=128, "
                          "B=16384/S) in place of the long-context one (for per-length profiles)")
+    ap.add_argument("--head-dim", type=int, default=128, choices=(16, 32, 64, 128),
+                    help="time the workload at this head dim in place of 128 (for per-head-dim "
+                         "profiles; the line then names that head dim)")
     return ap.parse_args()
 
 
@@ -632,6 +635,10 @@ def main():
     case = W.long_case()
     if args.seq:
         case = next(c for c in W.sweep_cases() if c.Sq == args.seq and c.causal)
+    if args.head_dim != case.D:
+        import dataclasses
+        case = dataclasses.replace(case, name=f"{case.name}_d{args.head_dim}", D=args.head_dim)
+    default_workload = not args.seq and case.D == 128
     x, dev = make_device_inputs(case, torch)
     r = time_path(fa, torch, case, dev, args.steps, args.warmup, flush, sensors)
     med, mean = r["median"], r["mean"]
@@ -652,7 +659,7 @@ def main():
     dom = max(units, key=lambda n: mean[n])
     achieved = units[dom] * unit / (mean[dom] * 1e-3) / 1e12
     line = {
-        "metric": "attention TFLOP/s fwd+bwd (fp16, causal, D=128)",
+        "metric": f"attention TFLOP/s fwd+bwd (fp16, causal, D={case.D})",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -680,7 +687,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": MFMA_PEAK_F16, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_F16, 4),
-                     "traffic": measured_traffic(dom)},
+                     # bytes recorded for the long-context D=128 workload only
+                     "traffic": measured_traffic(dom) if default_workload else None},
         "tiles": tiles_used(fa, case),
         "environment": env,
         "clock_power": {"during_timed_steps": r["sensors"]},
