@@ -256,11 +256,14 @@ class Flusher:
 
 
 def time_path(fa, torch, case, dev, steps, warmup, flush, sensors=None, min_warm_s=0.0):
-    """Time `steps` full passes.  Each pass: a cache flush (untimed), then
-    events around the forward and each backward stage on the stream the
-    kernels run on (torch's current stream).  Returns medians, means and the
-    per-step list, the wall time of the timed loop, and the outputs of the
-    last pass."""
+    """Time `steps` full passes twice over, interleaved.  Each pass: a cache
+    flush (untimed), then the forward and the backward stages on the stream
+    the kernels run on (torch's current stream).  A step's time comes from
+    passes with one event before the forward and one after the last stage
+    only (an event recorded between kernels costs the stream about 5 us);
+    the per-kernel times from the interleaved passes with an event after
+    every kernel.  Returns medians, means and the per-step list, the wall
+    time of the timed loop, and the outputs of the last pass."""
     B, H, Sq, Sk, D = case.B, case.H, case.Sq, case.Sk, case.D
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     o = torch.empty_like(q)
@@ -269,18 +272,18 @@ def time_path(fa, torch, case, dev, steps, warmup, flush, sensors=None, min_warm
     delta = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
     sc = case.scale
 
-    def step(ev=None):
+    def step(ev=None, ends_only=False):
         if ev is not None:
             ev[0].record()
         fa.fa_fwd(q, k, v, case.causal, sc, out=o, lse=lse)
-        if ev is not None:
+        if ev is not None and not ends_only:
             ev[1].record()
         # rowsum(dO.O) (nothing where the dQ kernel forms it), dQ, dK/dV: the
         # order fa_bwd runs them in.
         for j, stage in enumerate((0, 2, 1)):
             fa.fa_bwd_stage(stage, -1, q, k, v, o, do, lse, case.causal, sc, dq=dq, dk=dk, dv=dv,
                             delta=delta)
-            if ev is not None:
+            if ev is not None and (not ends_only or j == 2):
                 ev[2 + j].record()
 
     t_end = time.perf_counter() + min_warm_s
@@ -293,10 +296,13 @@ def time_path(fa, torch, case, dev, steps, warmup, flush, sensors=None, min_warm
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    ends = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     if sensors is not None:
         sensors.start()
     t0 = time.perf_counter()
     for i in range(steps):
+        flush()
+        step(ends[i], ends_only=True)
         flush()
         step(evs[i])
     torch.cuda.synchronize()
@@ -304,7 +310,8 @@ def time_path(fa, torch, case, dev, steps, warmup, flush, sensors=None, min_warm
     sens = sensors.stop() if sensors is not None else None
     names = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv")
     per = {n: [ev[j].elapsed_time(ev[j + 1]) for ev in evs] for j, n in enumerate(names)}
-    per["step"] = [ev[0].elapsed_time(ev[4]) for ev in evs]
+    per["step"] = [ev[0].elapsed_time(ev[4]) for ev in ends]
+    per["step_with_kernel_events"] = [ev[0].elapsed_time(ev[4]) for ev in evs]
     res = {
         "median": {n: statistics.median(v) for n, v in per.items()},
         "mean": {n: sum(v) / len(v) for n, v in per.items()},
@@ -369,7 +376,7 @@ def length_sweep(fa, torch, steps, warmup, flush, keep_samples):
                     "fwdbwd_frac_of_peak": round(fb_tf / MFMA_PEAK_F16, 4),
                     "ms_per_step": round(med["step"], 4),
                     "ms_per_step_min_max": [round(min(r["step_ms"]), 4), round(max(r["step_ms"]), 4)],
-                    "kernel_ms": {n: round(v, 4) for n, v in med.items() if n != "step"},
+                    "kernel_ms": {n: round(v, 4) for n, v in med.items() if not n.startswith("step")},
                     "tiles": {k: v["id"] for k, v in tiles_used(fa, sc).items()}})
         if keep_samples:
             kh = [(0, 0), (sc.B - 1, sc.H - 1)] if sc.Sq < 8192 else [(sc.B - 1, sc.H - 1)]
@@ -674,16 +681,20 @@ def main():
         "config": {"workload": (f"{'long-context' if not args.seq else 'length-sweep'} causal fp16 "
                                 f"attention fwd+bwd, B={case.B} H={case.H} S={case.Sq} D={case.D}"),
                    "B": case.B, "H": case.H, "S": case.Sq, "D": case.D, "causal": True},
-        "timing": {"statistic": "median of per-step HIP-event times",
+        "timing": {"statistic": "median of per-step HIP-event times (events before the forward and "
+                                "after the last backward stage only; per-kernel times from "
+                                "interleaved steps with an event after every kernel)",
+                   "ms_per_step_with_kernel_events": round(med["step_with_kernel_events"], 4),
                    "flush_before_each_step_bytes": 0 if args.no_flush else FLUSH_BYTES,
                    "ms_per_step_mean": round(mean["step"], 4),
                    "ms_per_step_min_max": [round(min(r["step_ms"]), 4), round(max(r["step_ms"]), 4)],
-                   "timed_loop_wall_s_incl_flush": round(r["wall_s"], 4)},
+                   "timed_loop_wall_s_incl_flush": round(r["wall_s"], 4),
+                   "passes_in_timed_loop": 2 * args.steps},
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_frac_of_peak": round(fwd_tf / MFMA_PEAK_F16, 4),
         "fwdbwd_frac_of_peak": round(value / MFMA_PEAK_F16, 4),
-        "kernel_ms": {n: round(v, 4) for n, v in med.items() if n != "step"},
-        "kernel_ms_mean": {n: round(v, 4) for n, v in mean.items() if n != "step"},
+        "kernel_ms": {n: round(v, 4) for n, v in med.items() if not n.startswith("step")},
+        "kernel_ms_mean": {n: round(v, 4) for n, v in mean.items() if not n.startswith("step")},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": MFMA_PEAK_F16, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_F16, 4),
@@ -704,7 +715,7 @@ def main():
         line["bf16"] = {"fwd_tflops": round(ff / (br["median"]["fwd"] * 1e-3) / 1e12, 2),
                         "fwdbwd_tflops": round(3.5 * ff / (br["median"]["step"] * 1e-3) / 1e12, 2),
                         "ms_per_step": round(br["median"]["step"], 4), "steps": bsteps,
-                        "kernel_ms": {n: round(v, 4) for n, v in br["median"].items() if n != "step"}}
+                        "kernel_ms": {n: round(v, 4) for n, v in br["median"].items() if not n.startswith("step")}}
         del bdev, br
     if not args.no_d64:
         # Secondary figure: the same workload at head dim 64 (the mid
@@ -720,7 +731,7 @@ def main():
                        "fwd_tflops": round(dff / (dr["median"]["fwd"] * 1e-3) / 1e12, 2),
                        "fwdbwd_tflops": round(3.5 * dff / (dr["median"]["step"] * 1e-3) / 1e12, 2),
                        "ms_per_step": round(dr["median"]["step"], 4), "steps": dsteps,
-                       "kernel_ms": {n: round(v, 4) for n, v in dr["median"].items() if n != "step"},
+                       "kernel_ms": {n: round(v, 4) for n, v in dr["median"].items() if not n.startswith("step")},
                        "tiles": tiles_used(fa, dcase)}
         del ddev, dr
     line["memory"] = peak_memory(torch, case, dev)
