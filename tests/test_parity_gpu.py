@@ -153,6 +153,33 @@ BOTTOM_RIGHT = [
 ]
 
 
+def _random_cases(n=24, seed=1234):
+    """Seeded random shapes over every supported axis at once: batch, heads,
+    ragged Sq and Sk (1..700, independent), head dim, dtype, mask (none,
+    top-left, bottom-right) and storage layout."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([16, 32, 64, 128]))
+        dname = str(rng.choice(["f16", "bf16", "f32"]))
+        causal = int(rng.integers(0, 3))
+        Sq, Sk = int(rng.integers(1, 701)), int(rng.integers(1, 701))
+        if causal == 1:
+            Sk = max(Sk, Sq)  # top-left causal: every query row sees key 0
+        layout = str(rng.choice(["bhsd", "bshd"]))
+        out.append(W.Case(f"rand{i}_{dname}_D{D}_c{causal}_{Sq}x{Sk}_{layout}",
+                          int(rng.integers(1, 3)), int(rng.integers(1, 4)), Sq, Sk, D, dname, causal,
+                          seed=1000 + i, layout=layout))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: c.name)
+def test_random_shapes(case):
+    """Seeded random shapes, compared element by element with the oracle."""
+    x, got = run_case(case)
+    check_full(case, x, got)
+
+
 @pytest.mark.parametrize("case", BOTTOM_RIGHT, ids=lambda c: c.name)
 def test_bottom_right_causal(case):
     """causal = 2: query i sees keys j <= i + Sk - Sq; rows with no visible key
